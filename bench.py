@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the SpargeAttention2 hot path on one MI355X.
+
+One step = the whole path on one batch: block mask (pool, P-bar, Top-k U Top-p, lists),
+block-sparse forward, block-sparse backward (preprocess, dK/dV pass, dQ pass). Default
+workload: the Wan2.1-1.3B-shaped 480p attention (B=1, H=12, N=32760, D=128, bf16,
+b_q=128, b_kv=64, k=2%, p tuned to 95% block sparsity) on seeded synthetic inputs.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+  value        effective TFLOP/s of the whole step: (4 d A + 10 d A) / step time, where A
+               is the kept query x key area in real tokens (forward 4dA, backward 10dA)
+  roofline     the dominant kernel's algorithmic FLOPs per launch / its event-timed
+               average duration, against the 2.5 PFLOP/s dense bf16 MFMA peak
+  cpu_baseline the float64 oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse attn fwd+bwd ms & eff. TFLOPS at N=32760, 95% sparsity; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kept_area(mask, n, bq, bkv):
+    """Sum over kept (i, j) of rows(i) * cols(j), in real tokens. mask: bool [B,H,Tm,Tn]."""
+    import numpy as np
+    tm, tn = mask.shape[-2:]
+    rows = np.minimum(n, (np.arange(tm) + 1) * bq) - np.arange(tm) * bq
+    cols = np.minimum(n, (np.arange(tn) + 1) * bkv) - np.arange(tn) * bkv
+    return int(np.einsum("bhij,i,j->", mask.astype(np.int64), rows, cols))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b_480p")
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle parity check")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--dense-reps", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus "
+              f"{args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_spa2_amd as spa2
+    from gen import configs
+
+    torch.cuda.set_device(0)
+    w = configs.params(args.workload)
+    B, H, N, D, bq, bkv = w["B"], w["H"], w["N"], w["D"], w["BQ"], w["BKV"]
+    kf, pf = w["k"], w["p"]
+    t0 = time.time()
+    inp = configs.make_inputs(args.workload)
+    log(f"[bench] inputs {args.workload} B={B} H={H} N={N} D={D} drawn in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v, do = (dev(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    bm = spa2.BlockMask.empty(B, H, N, bq, bkv, q.device)
+    mws = torch.empty(spa2.mask_workspace_size(q, bq, bkv), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dvec = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    o_f32 = torch.empty(q.shape, dtype=torch.float32, device="cuda")  # unrounded O for bwd
+
+    def stage_mask():
+        spa2.mask(q, k, kf, pf, bq, bkv, out=bm, workspace=mws)
+
+    def stage_fwd():
+        spa2.fwd(q, k, v, bm, out=(o, lse), o_f32=o_f32)
+
+    def stage_prep():
+        spa2.bwd_prep(o, do, dvec, bq, bkv, o_f32=o_f32)
+
+    def stage_dkdv():
+        spa2.bwd_dkdv(q, k, v, lse, do, dvec, bm, dk, dv)
+
+    def stage_dq():
+        spa2.bwd_dq(q, k, v, lse, do, dvec, bm, dq)
+
+    stages = [("mask", stage_mask), ("fwd", stage_fwd), ("bwd_prep", stage_prep),
+              ("bwd_dkdv", stage_dkdv), ("bwd_dq", stage_dq)]
+
+    for _ in range(args.warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    gmask = bm.mask.cpu().numpy().astype(bool)
+    area = kept_area(gmask, N, bq, bkv)
+    kept_frac = float(gmask.mean())
+    flops_fwd = 4.0 * D * area
+    flops_bwd = 10.0 * D * area
+
+    parity = None
+    if not args.no_check:
+        parity = check_parity(inp, w, gmask, o, lse, dq, dk, dv)
+        log(f"[bench] parity {parity}")
+
+    # ---- timed region: exactly `steps` steps, events around every stage
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            evs[s][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    per_stage = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1])
+                                      for s in range(args.steps)]))
+                 for i, (name, _) in enumerate(stages)}
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step; stages {per_stage}")
+
+    # ---- dense baseline: the same kernels with every block kept (mask = NULL)
+    dense = {}
+    if args.dense_reps > 0:
+        od, ld = torch.empty_like(q), torch.empty_like(lse)
+        spa2.fwd(q, k, v, None, bq, bkv, out=(od, ld))
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        for _ in range(args.dense_reps):
+            spa2.fwd(q, k, v, None, bq, bkv, out=(od, ld))
+        e1.record(stream)
+        for _ in range(args.dense_reps):
+            spa2.bwd(q, k, v, od, ld, do, None, bq, bkv, out=(dq, dk, dv))
+        e2.record(stream)
+        torch.cuda.synchronize()
+        dense = dict(fwd_ms=e0.elapsed_time(e1) / args.dense_reps,
+                     bwd_ms=e1.elapsed_time(e2) / args.dense_reps)
+        log(f"[bench] dense {dense}")
+
+    sparse_fb = per_stage["fwd"] + per_stage["bwd_prep"] + per_stage["bwd_dkdv"] + per_stage["bwd_dq"]
+    kernel_flops = {"fwd": flops_fwd, "bwd_dkdv": 8.0 * D * area, "bwd_dq": 2.0 * D * area}
+    dom = max(kernel_flops, key=lambda n: per_stage[n])
+    achieved = kernel_flops[dom] / (per_stage[dom] * 1e-3) / 1e12
+    roofline = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2),
+                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    flops_per_launch=kernel_flops[dom], ms_per_launch=round(per_stage[dom], 4))
+    mask_bytes = 2.0 * B * H * N * D * q.element_size()  # Q and K read once
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(inp, w, gmask, flops_fwd + flops_bwd)
+        log(f"[bench] cpu baseline {cpu}")
+
+    value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inp.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded generator, Wan2.1-1.3B 480p attention shape)",
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "D": D, "bq": bq,
+                   "bkv": bkv, "k": kf, "p": pf, "kept_fraction": round(kept_frac, 6),
+                   "kept_area_tokens2": area},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_ms": {k_: round(v_, 4) for k_, v_ in per_stage.items()},
+        "fwd_bwd_ms": round(sparse_fb, 4),
+        "fwd_bwd_tflops": round((flops_fwd + flops_bwd) / (sparse_fb * 1e-3) / 1e12, 2),
+        "fwd_tflops": round(flops_fwd / (per_stage["fwd"] * 1e-3) / 1e12, 2),
+        "mask_hbm": {"bytes": mask_bytes,
+                     "GB/s": round(mask_bytes / (per_stage["mask"] * 1e-3) / 1e9, 1),
+                     "frac": round(mask_bytes / (per_stage["mask"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "dense_ms": {k_: round(v_, 3) for k_, v_ in dense.items()},
+        "speedup_vs_dense": ({
+            "fwd_kernel": round(dense["fwd_ms"] / per_stage["fwd"], 2),
+            "fwd_incl_mask": round(dense["fwd_ms"] / (per_stage["fwd"] + per_stage["mask"]), 2),
+            "fwd_bwd_incl_mask": round((dense["fwd_ms"] + dense["bwd_ms"]) / ms_step, 2),
+        } if dense else None),
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def check_parity(inp, w, gmask, o, lse, dq, dk, dv):
+    """Masks of every head against the oracle; O, LSE and dQ of sampled query blocks and
+    dK, dV of sampled key blocks of the first and last head."""
+    import numpy as np
+
+    import oracle
+
+    B, H, N, D, bq, bkv = w["B"], w["H"], w["N"], w["D"], w["BQ"], w["BKV"]
+    t0 = time.time()
+    mism = band = 0
+    masks = {}
+    for b in range(B):
+        for h in range(H):
+            m, info = oracle.block_mask_head(inp.head_f64("q", b, h), inp.head_f64("k", b, h),
+                                             bq, bkv, w["k"], w["p"], with_info=True)
+            masks[(b, h)] = m
+            diff = np.argwhere(m != gmask[b, h])
+            for i, j in diff:
+                if j in set(info["rows"][i]["p_band"]):
+                    band += 1
+                else:
+                    mism += 1
+    assert mism == 0, f"mask mismatches outside the p band: {mism}"
+    to64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    on, ln, dqn, dkn, dvn = to64(o), lse.cpu().numpy(), to64(dq), to64(dk), to64(dv)
+    errs = {}
+    tm, tn = gmask.shape[-2:]
+    for h in sorted({0, H - 1}):
+        m = masks[(0, h)]
+        q, k, v, do = (inp.head_f64(x, 0, h) for x in ("q", "k", "v", "do"))
+        qblocks = [0, tm // 3, tm - 1]
+        kblocks = [1, tn // 2, tn - 1]
+        rows = sorted(set(qblocks) | {i for j in kblocks for i in np.flatnonzero(m[:, j])})
+        o_ref, lse_ref = oracle.attn_fwd_head(q, k, v, m, bq, bkv, rows=qblocks)
+        dq_ref, dk_ref, dv_ref = oracle.attn_bwd_head(q, k, v, do, m, bq, bkv, rows=rows)
+        qr = np.concatenate([np.arange(i * bq, min(N, (i + 1) * bq)) for i in qblocks])
+        kr = np.concatenate([np.arange(j * bkv, min(N, (j + 1) * bkv)) for j in kblocks])
+        for name, got, ref in (("O", on[0, h][qr], o_ref[qr]), ("dQ", dqn[0, h][qr], dq_ref[qr]),
+                               ("dK", dkn[0, h][kr], dk_ref[kr]), ("dV", dvn[0, h][kr], dv_ref[kr])):
+            e = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+            errs[name] = max(errs.get(name, 0.0), e)
+        errs["LSE_abs"] = max(errs.get("LSE_abs", 0.0), float(np.abs(ln[0, h][qr] - lse_ref[qr]).max()))
+    tol = 2e-2 if inp.dtype == "bf16" else 1e-4
+    for name in ("O", "dQ", "dK", "dV"):
+        assert errs[name] <= tol, f"{name} rel-L2 {errs[name]}"
+    return {"mask_mismatch_outside_p_band": mism, "mask_p_band_flips": band,
+            "rel_l2_sampled": {k_: float(f"{v_:.3e}") for k_, v_ in errs.items()},
+            "seconds": round(time.time() - t0, 1)}
+
+
+def cpu_baseline(inp, w, gmask, total_flops, budget_s=20.0):
+    """The float64 oracle on a bounded sample of the workload, extrapolated to the whole
+    step: the mask of whole heads plus forward and backward of evenly spaced query
+    blocks, repeated head by head until about `budget_s` seconds have passed."""
+    import numpy as np
+
+    import oracle
+
+    B, H, N, D, bq, bkv = w["B"], w["H"], w["N"], w["D"], w["BQ"], w["BKV"]
+    tm = gmask.shape[2]
+    stride = 4
+    t_mask = t_fb = 0.0
+    heads = 0
+    qblocks_done = 0
+    t_start = time.time()
+    for h in range(H):
+        q, k, v, do = (inp.head_f64(x, 0, h) for x in ("q", "k", "v", "do"))
+        t0 = time.time()
+        m = oracle.block_mask_head(q, k, bq, bkv, w["k"], w["p"])
+        t1 = time.time()
+        rows = list(range(h % stride, tm, stride))
+        oracle.attn_fwd_head(q, k, v, m, bq, bkv, rows=rows)
+        oracle.attn_bwd_head(q, k, v, do, m, bq, bkv, rows=rows)
+        t2 = time.time()
+        t_mask += t1 - t0
+        t_fb += t2 - t1
+        heads += 1
+        qblocks_done += len(rows)
+        if time.time() - t_start > budget_s:
+            break
+    est = (t_mask / heads) * B * H + (t_fb / qblocks_done) * B * H * tm
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": round(total_flops / est / 1e12, 6), "unit": "TFLOP/s",
+            "cores": min(threads, len(os.sched_getaffinity(0))), "kind": "oracle",
+            "sample": (f"float64 oracle: mask of {heads} whole head(s) and forward+backward of "
+                       f"every {stride}th query block of those heads ({qblocks_done} of "
+                       f"{B * H * tm} blocks), extrapolated to the full step "
+                       f"({est:.1f} s estimated)"),
+            "seconds_measured": round(time.time() - t_start, 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+// C ABI of the SpargeAttention2 hot path: argument validation and dispatch.
+// Every check runs before the first HIP call, so an invalid call writes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/spa2.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char* where, hipError_t e) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+}
+
+int blocks(int n, int b) { return (n + b - 1) / b; }
+
+spa2_status check_desc(const spa2_desc* d, spa2::Shape* out) {
+  if (!d) return SPA2_E_NULL;
+  if (d->dtype != SPA2_F32 && d->dtype != SPA2_BF16) return SPA2_E_DTYPE;
+  if (d->B < 1 || d->H < 1 || d->N < 1 || d->N > (1 << 20)) return SPA2_E_SHAPE;
+  if ((long long)d->B * d->H > (1LL << 24)) return SPA2_E_SHAPE;
+  if (d->D != 64 && d->D != 128) return SPA2_E_SHAPE;
+  if (d->BQ != 64 && d->BQ != 128) return SPA2_E_SHAPE;
+  if (d->BKV != 64) return SPA2_E_SHAPE;
+  const int tn = blocks(d->N, d->BKV);
+  if (tn > spa2::kMaxSort) return SPA2_E_SHAPE;
+  *out = spa2::Shape{d->B, d->H, d->N, d->D, d->BQ, d->BKV, d->dtype, blocks(d->N, d->BQ), tn};
+  return SPA2_OK;
+}
+
+spa2_status check_fracs(double k, double p) {
+  if (std::isnan(k) || std::isnan(p)) return SPA2_E_PARAM;
+  if (k < 0.0 || k > 1.0 || p < 0.0 || p > 1.0) return SPA2_E_PARAM;
+  if (k == 0.0 && p == 0.0) return SPA2_E_PARAM;
+  return SPA2_OK;
+}
+
+// Top-k count: ceil(k * T_n - 1e-9) clamped to [0, T_n].
+int topk_count(double k, int tn) {
+  const double c = std::ceil(k * (double)tn - 1e-9);
+  if (c < 0.0) return 0;
+  if (c > (double)tn) return tn;
+  return (int)c;
+}
+
+spa2_status check_blockmask(const spa2_blockmask* m, bool need_lists) {
+  if (!m || !m->mask) return SPA2_E_NULL;
+  if (need_lists && (!m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
+  return SPA2_OK;
+}
+
+size_t mask_ws_bytes(const spa2::Shape& s) {
+  const size_t bh = (size_t)s.BH();
+  return bh * ((size_t)(s.Tm + s.Tn) * s.D + (size_t)s.Tm * s.Tn) * sizeof(double);
+}
+
+spa2_status hip_status(const char* where, hipError_t e) {
+  if (e == hipSuccess) return SPA2_OK;
+  set_error(where, e);
+  return SPA2_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spa2_status_str(spa2_status s) {
+  switch (s) {
+    case SPA2_OK: return "ok";
+    case SPA2_E_NULL: return "a required pointer is NULL";
+    case SPA2_E_SHAPE: return "shape out of the supported range";
+    case SPA2_E_DTYPE: return "unknown dtype";
+    case SPA2_E_PARAM: return "k/p fraction outside [0, 1], NaN, or both zero";
+    case SPA2_E_WORKSPACE: return "workspace missing or too small";
+    case SPA2_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* spa2_last_error(void) { return g_last_error; }
+
+int32_t spa2_num_blocks(int32_t n, int32_t block) {
+  if (n < 1 || block < 1) return 0;
+  return blocks(n, block);
+}
+
+spa2_status spa2_pool(const spa2_desc* desc, const void* q, const void* k, double* qbar,
+                      double* kbar, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k || !qbar || !kbar) return SPA2_E_NULL;
+  return hip_status("pool", spa2::launch_pool(s, q, k, qbar, kbar, (hipStream_t)stream));
+}
+
+spa2_status spa2_mask_workspace_size(const spa2_desc* desc, size_t* bytes) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!bytes) return SPA2_E_NULL;
+  *bytes = mask_ws_bytes(s);
+  return SPA2_OK;
+}
+
+spa2_status spa2_mask(const spa2_desc* desc, const void* q, const void* k, double k_frac,
+                      double p_frac, const spa2_blockmask* out, double* pbar_out,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k) return SPA2_E_NULL;
+  if ((st = check_blockmask(out, true)) != SPA2_OK) return st;
+  if ((st = check_fracs(k_frac, p_frac)) != SPA2_OK) return st;
+  if (!workspace || ws_bytes < mask_ws_bytes(s)) return SPA2_E_WORKSPACE;
+
+  const hipStream_t hs = (hipStream_t)stream;
+  double* qbar = (double*)workspace;
+  double* kbar = qbar + (size_t)s.BH() * s.Tm * s.D;
+  double* scores = kbar + (size_t)s.BH() * s.Tn * s.D;
+  if ((st = hip_status("pool", spa2::launch_pool(s, q, k, qbar, kbar, hs))) != SPA2_OK) return st;
+  if ((st = hip_status("scores", spa2::launch_scores(s, qbar, kbar, scores, hs))) != SPA2_OK)
+    return st;
+  if ((st = hip_status("select", spa2::launch_select(s, scores, true, pbar_out,
+                                                     topk_count(k_frac, s.Tn), p_frac, *out,
+                                                     hs))) != SPA2_OK)
+    return st;
+  return hip_status("cols", spa2::launch_cols(s, *out, hs));
+}
+
+spa2_status spa2_select(const spa2_desc* desc, const double* pbar, double k_frac, double p_frac,
+                        const spa2_blockmask* out, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!pbar) return SPA2_E_NULL;
+  if ((st = check_blockmask(out, true)) != SPA2_OK) return st;
+  if ((st = check_fracs(k_frac, p_frac)) != SPA2_OK) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  if ((st = hip_status("select", spa2::launch_select(s, pbar, false, nullptr,
+                                                     topk_count(k_frac, s.Tn), p_frac, *out,
+                                                     hs))) != SPA2_OK)
+    return st;
+  return hip_status("cols", spa2::launch_cols(s, *out, hs));
+}
+
+spa2_status spa2_mask_lists(const spa2_desc* desc, const spa2_blockmask* m, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if ((st = check_blockmask(m, true)) != SPA2_OK) return st;
+  const hipStream_t hs = (hipStream_t)stream;
+  if ((st = hip_status("rows", spa2::launch_rows(s, *m, hs))) != SPA2_OK) return st;
+  return hip_status("cols", spa2::launch_cols(s, *m, hs));
+}
+
+spa2_status spa2_fwd(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                     const spa2_blockmask* m, void* o, float* lse, float* o_f32,
+                     void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k || !v || !o || !lse) return SPA2_E_NULL;
+  if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
+  return hip_status("fwd", spa2::launch_fwd(s, q, k, v, m ? m->row_cnt : nullptr,
+                                            m ? m->row_idx : nullptr, o, lse, o_f32,
+                                            (hipStream_t)stream));
+}
+
+spa2_status spa2_bwd_workspace_size(const spa2_desc* desc, size_t* bytes) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!bytes) return SPA2_E_NULL;
+  *bytes = (size_t)s.BH() * s.N * sizeof(float);
+  return SPA2_OK;
+}
+
+spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                     const void* o, const float* o_f32, const float* lse, const void* dout,
+                     const spa2_blockmask* m, void* dq, void* dk, void* dv, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPA2_E_NULL;
+  if (m && (!m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
+  if (!workspace || ws_bytes < (size_t)s.BH() * s.N * sizeof(float)) return SPA2_E_WORKSPACE;
+  return hip_status("bwd", spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, dk, dv,
+                                            (float*)workspace, spa2::kBwdAll,
+                                            (hipStream_t)stream));
+}
+
+spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f32,
+                          const void* dout, float* dvec, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!o || !dout || !dvec) return SPA2_E_NULL;
+  return hip_status("bwd_prep", spa2::launch_bwd(s, nullptr, nullptr, nullptr, o, o_f32, nullptr, dout,
+                                                 nullptr, nullptr, nullptr, nullptr, dvec,
+                                                 spa2::kBwdPrep, (hipStream_t)stream));
+}
+
+spa2_status spa2_bwd_dkdv(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, const float* dvec,
+                          const spa2_blockmask* m, void* dk, void* dv, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k || !v || !lse || !dout || !dvec || !dk || !dv) return SPA2_E_NULL;
+  if (m && (!m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
+  return hip_status("bwd_dkdv", spa2::launch_bwd(s, q, k, v, nullptr, nullptr, lse, dout, m, nullptr, dk,
+                                                 dv, (float*)dvec, spa2::kBwdDkdv,
+                                                 (hipStream_t)stream));
+}
+
+spa2_status spa2_bwd_dq(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                        const float* lse, const void* dout, const float* dvec,
+                        const spa2_blockmask* m, void* dq, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k || !v || !lse || !dout || !dvec || !dq) return SPA2_E_NULL;
+  if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
+  return hip_status("bwd_dq", spa2::launch_bwd(s, q, k, v, nullptr, nullptr, lse, dout, m, dq, nullptr,
+                                               nullptr, (float*)dvec, spa2::kBwdDq,
+                                               (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,250 @@
+// Block-sparse attention forward on gfx950.
+//
+// Method (SpargeAttention2, paper.rainbus.top summary, "方法步骤详情" step 4; "前置知识",
+// block-sparse attention): for each kept block pair (i, j), S_ij = Q_i K_j^T / sqrt(D),
+// the softmax is taken online over the kept key blocks of row i only, and O_i
+// accumulates P_ij V_j. Masked pairs are skipped entirely: their K/V tiles are never
+// fetched.
+//
+// One workgroup (4 waves) per query block. Wave w owns BQ/4 query rows. Per kept key
+// block the workgroup stages K_j and V_j (64 x D) into a double-buffered, swizzled LDS
+// tile while the previous block is being computed. Scores are computed transposed,
+// S^T = K Q^T (operand A = K rows from LDS, operand B = Q held in registers), so each
+// lane owns one query column and the online-softmax state is lane local (the row max
+// needs the 4 lanes that share the column). P^T leaves the accumulators directly as the
+// B operand of O^T = V^T P^T; V^T comes from row-major LDS through transpose reads.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace spa2 {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* o_f32;  // optional unrounded copy of O
+  const int32_t* row_cnt;  // nullptr: dense
+  const int32_t* row_idx;
+  int N, Tm, Tn;
+  float scale_log2;  // log2(e) / sqrt(D)
+};
+
+template <typename T, int D, int BQ>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+  using E = Elem<T>;
+  using F = typename E::frag;
+  constexpr int BKV = 64;
+  constexpr int QT = BQ / 64;  // 16-row query tiles per wave
+  constexpr int KS = D / 32;   // reduction steps over the head dimension
+  constexpr int DT = D / 16;   // 16-wide output column tiles
+  using KV = Tile<T, BKV, D>;
+  constexpr int CPR = KV::kChunks;       // 16-byte chunks per K/V row
+  constexpr int CH = BKV * CPR / 256;    // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) char smem[2][2][KV::kBytes];
+
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, g = l >> 4, c16 = l & 15;
+  const int bh = blockIdx.x / a.Tm, qb = blockIdx.x % a.Tm;
+  const int N = a.N;
+  const size_t head = (size_t)bh * N * D;
+  const T* Q = (const T*)a.q + head;
+  const T* K = (const T*)a.k + head;
+  const T* V = (const T*)a.v + head;
+  const int q0 = qb * BQ + w * 16 * QT;
+
+  // Q as the B operand: lane -> query q0 + 16 qt + c16, dims 32 ks + 8 g .. +8
+  F qf[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int row = q0 + qt * 16 + c16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[qt][ks] = row < N ? load_row8<T>(Q + (size_t)row * D + ks * 32 + 8 * g) : E::zero();
+  }
+
+  const bool dense = a.row_cnt == nullptr;
+  const int cnt = dense ? a.Tn : a.row_cnt[blockIdx.x];
+  const int32_t* list = dense ? nullptr : a.row_idx + (size_t)blockIdx.x * a.Tn;
+
+  u32x4 kr[CH], vr[CH];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
+      const int key = j * BKV + row;
+      if (key < N) {
+        kr[c] = *reinterpret_cast<const u32x4*>(K + (size_t)key * D + ch * (16 / sizeof(T)));
+        vr[c] = *reinterpret_cast<const u32x4*>(V + (size_t)key * D + ch * (16 / sizeof(T)));
+      } else {
+        kr[c] = u32x4{0, 0, 0, 0};
+        vr[c] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
+      KV::store_chunk(smem[buf][0], row, ch, kr[c]);
+      KV::store_chunk(smem[buf][1], row, ch, vr[c]);
+    }
+  };
+
+  f32x4 oacc[DT][QT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[QT], lrow[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    mrow[qt] = -INFINITY;
+    lrow[qt] = 0.f;
+  }
+
+  if (cnt > 0) {
+    gload(dense ? 0 : list[0]);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < cnt; ++t) {
+    const int j = dense ? t : list[t];
+    const int buf = t & 1;
+    if (t + 1 < cnt) gload(dense ? t + 1 : list[t + 1]);
+    const char* Kb = smem[buf][0];
+    const char* Vb = smem[buf][1];
+
+    // S^T = K Q^T : s[kt][qt] lane holds S^T[key 16 kt + 4 g + e][query 16 qt + c16]
+    f32x4 s[4][QT];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const F ka = KV::read_row8(Kb, kt * 16 + c16, ks * 32 + 8 * g);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[kt][qt] = E::mma(ka, qf[qt][ks], s[kt][qt]);
+      }
+    }
+    // keys past N exist only in the last, partial key block
+    if ((j + 1) * BKV > N) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j * BKV + kt * 16 + 4 * g + e >= N)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) s[kt][qt][e] = -INFINITY;
+    }
+
+    // online softmax, per query column (base-2 exponent with the scale folded in)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[kt][qt][e]);
+      mx = max4(mx) * a.scale_log2;
+      const float mnew = fmaxf(mrow[qt], mx);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mref);
+      mrow[qt] = mnew;
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[kt][qt][e] * a.scale_log2 - mref);
+          s[kt][qt][e] = p;
+          ls += p;
+        }
+      lrow[qt] = lrow[qt] * alpha + ls;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+    }
+
+    // O^T += V^T P^T over the block's 64 keys, 32 at a time
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      F pf[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) pf[qt] = E::pack(s[2 * u][qt], s[2 * u + 1][qt]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        F va;
+        KV::read_col4(Vb, 32 * u, dt * 16, va, 0);
+        KV::read_col4(Vb, 32 * u + 16, dt * 16, va, 1);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = E::mma(va, pf[qt], oacc[dt][qt]);
+      }
+    }
+
+    if (t + 1 < cnt) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: normalise, store O rows and LSE
+  T* O = (T*)a.o + head;
+  float* lse = a.lse + (size_t)bh * N;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int row = q0 + qt * 16 + c16;
+    const float lt = sum4(lrow[qt]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row < N) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        T outv[4];
+        f32x4 of;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          of[e] = oacc[dt][qt][e] * inv;
+          outv[e] = (T)of[e];
+        }
+        if (a.o_f32)
+          *reinterpret_cast<f32x4*>(a.o_f32 + head + (size_t)row * D + dt * 16 + 4 * g) = of;
+        T* dst = O + (size_t)row * D + dt * 16 + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dst) = bf16x4{outv[0], outv[1], outv[2], outv[3]};
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{outv[0], outv[1], outv[2], outv[3]};
+        }
+      }
+      if (g == 0) lse[row] = lt > 0.f ? (mrow[qt] + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                      const int32_t* row_cnt, const int32_t* row_idx, void* o, float* lse,
+                      float* o_f32, hipStream_t st) {
+  FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, s.N, s.Tm, s.Tn,
+            (float)(1.4426950408889634 / sqrt((double)s.D))};
+  const dim3 grid(s.BH() * s.Tm);
+#define SPA2_FWD(T, D, BQ) fwd_kernel<T, D, BQ><<<grid, 256, 0, st>>>(a)
+  if (s.dtype == SPA2_BF16) {
+    if (s.D == 64) {
+      if (s.BQ == 64) SPA2_FWD(bf16, 64, 64); else SPA2_FWD(bf16, 64, 128);
+    } else {
+      if (s.BQ == 64) SPA2_FWD(bf16, 128, 64); else SPA2_FWD(bf16, 128, 128);
+    }
+  } else {
+    if (s.D == 64) {
+      if (s.BQ == 64) SPA2_FWD(float, 64, 64); else SPA2_FWD(float, 64, 128);
+    } else {
+      if (s.BQ == 64) SPA2_FWD(float, 128, 64); else SPA2_FWD(float, 128, 128);
+    }
+  }
+#undef SPA2_FWD
+  return hipGetLastError();
+}
+
+}  // namespace spa2

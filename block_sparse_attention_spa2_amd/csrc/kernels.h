@@ -1,0 +1,39 @@
+// Internal launch interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spa2.h"
+
+namespace spa2 {
+
+struct Shape {
+  int B, H, N, D, BQ, BKV, dtype;
+  int Tm, Tn;   // query / key block counts
+  int BH() const { return B * H; }
+};
+
+// Largest key-block count the selection kernel sorts (power of two).
+constexpr int kMaxSort = 4096;
+
+hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar,
+                       hipStream_t st);
+hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar, double* scores,
+                         hipStream_t st);
+// from_scores: src holds raw pooled scores (softmax applied here); else src holds P-bar.
+hipError_t launch_select(const Shape& s, const double* src, bool from_scores, double* pbar_out,
+                         int n_k, double p_frac, const spa2_blockmask& m, hipStream_t st);
+hipError_t launch_rows(const Shape& s, const spa2_blockmask& m, hipStream_t st);
+hipError_t launch_cols(const Shape& s, const spa2_blockmask& m, hipStream_t st);
+
+hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                      const int32_t* row_cnt, const int32_t* row_idx, void* o, float* lse,
+                      float* o_f32, hipStream_t st);
+// stage bits for launch_bwd
+constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7;
+hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
+                      const float* o_f32, const float* lse, const void* dout, const spa2_blockmask* m, void* dq,
+                      void* dk, void* dv, float* dvec, int stages, hipStream_t st);
+
+}  // namespace spa2

@@ -1,0 +1,167 @@
+/*
+ * spa2.h - C ABI of the SpargeAttention2 hot path on AMD MI355X (gfx950).
+ *
+ * The method (SpargeAttention2, arXiv 2602.13515) predicts a block mask from pooled
+ * queries and keys and then runs attention only over the kept blocks:
+ *   1. partition Q into T_m = ceil(N/BQ) query blocks and K, V into T_n = ceil(N/BKV)
+ *      key blocks (paper.rainbus.top summary, section "方法步骤详情", step 1);
+ *   2. mean-pool every block and form P-bar = softmax(pool(Q) pool(K)^T / sqrt(D)) per
+ *      row (same section, step 2);
+ *   3. keep key block j of query block i iff j is in Top-k(P-bar_i, k%) U
+ *      Top-p(P-bar_i, p%) (step 3; the union formula of section "技术新颖性");
+ *   4. compute attention for the kept block pairs only, with the softmax taken over
+ *      the kept keys (step 4; section "前置知识", block-sparse attention), forward and
+ *      backward (the sparse attention is trainable: abstract and section "核心方法").
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. Q, K, V, O, dO, dQ, dK, dV
+ *     are contiguous [B, H, N, D] in desc->dtype (D fastest). LSE is float [B, H, N].
+ *   - Descriptor structs are HOST memory and are read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
+ *     enqueues its kernels on that stream and returns without synchronising.
+ *   - The library never allocates device memory. Calls that need scratch space take a
+ *     caller-provided workspace whose size comes from the matching *_workspace_size call.
+ *   - Every argument is validated before any HIP call; an invalid call returns its error
+ *     code and writes nothing. A failed kernel launch returns SPA2_E_HIP (details from
+ *     spa2_last_error()). No C++ exception crosses this boundary.
+ *   - Supported: dtype F32 or BF16, D in {64, 128}, BQ in {64, 128}, BKV = 64,
+ *     1 <= N <= 2^20, B*H >= 1, T_n <= 4096.
+ *   - Attention is non-causal; the scale is 1/sqrt(D); LSE is the natural-log
+ *     log-sum-exp of the scaled scores over the kept keys. Outputs are rounded to the
+ *     input dtype (round to nearest even) from fp32 accumulators. A query row whose
+ *     block keeps no key block gets O = 0, LSE = -inf and dQ = 0.
+ */
+#ifndef SPA2_H
+#define SPA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPA2_OK = 0,
+  SPA2_E_NULL = 1,      /* a required pointer is NULL */
+  SPA2_E_SHAPE = 2,     /* B, H, N, D, BQ or BKV out of the supported range */
+  SPA2_E_DTYPE = 3,     /* unknown dtype */
+  SPA2_E_PARAM = 4,     /* k or p outside [0, 1], NaN, or both zero */
+  SPA2_E_WORKSPACE = 5, /* workspace NULL or smaller than the size call reports */
+  SPA2_E_HIP = 6        /* a HIP runtime call or kernel launch failed */
+} spa2_status;
+
+typedef enum { SPA2_F32 = 0, SPA2_BF16 = 1 } spa2_dtype;
+
+/* Problem shape. T_m = ceil(N/BQ), T_n = ceil(N/BKV); the last block of each may be
+ * partial (it covers the rows up to N only). */
+typedef struct {
+  int32_t B, H, N, D; /* batch, heads, tokens, head dimension */
+  int32_t BQ, BKV;    /* query and key block sizes (the method uses 128 and 64) */
+  int32_t dtype;      /* spa2_dtype of every [B, H, N, D] tensor */
+} spa2_desc;
+
+/* Block mask M-bar and its compacted lists, all device memory owned by the caller.
+ *   mask    uint8 [B, H, T_m, T_n]   1 = block pair kept
+ *   row_cnt int32 [B, H, T_m]        kept key blocks per query block
+ *   row_idx int32 [B, H, T_m, T_n]   their indices, ascending; entries past row_cnt unused
+ *   col_cnt int32 [B, H, T_n]        query blocks that keep each key block
+ *   col_idx int32 [B, H, T_n, T_m]   their indices, ascending; entries past col_cnt unused
+ * The forward reads the row lists; the backward reads both. */
+typedef struct {
+  uint8_t* mask;
+  int32_t* row_cnt;
+  int32_t* row_idx;
+  int32_t* col_cnt;
+  int32_t* col_idx;
+} spa2_blockmask;
+
+/* Text for a status code (static storage). */
+const char* spa2_status_str(spa2_status s);
+
+/* Detail of the last SPA2_E_HIP on the calling thread ("" if none; thread-local). */
+const char* spa2_last_error(void);
+
+/* Block counts for a descriptor (host only, no validation beyond positivity). */
+int32_t spa2_num_blocks(int32_t n, int32_t block);
+
+/* Step 2, pooling (rainbus summary, "方法步骤详情", step 2: pool(Q), pool(K)).
+ * qbar: double [B, H, T_m, D], kbar: double [B, H, T_n, D] (device, caller-owned):
+ * the arithmetic mean of each block's valid rows, accumulated in double. */
+spa2_status spa2_pool(const spa2_desc* desc, const void* q, const void* k, double* qbar,
+                      double* kbar, void* stream);
+
+/* Workspace bytes that spa2_mask needs for this descriptor (pooled vectors and the
+ * pooled score matrix, all double). */
+spa2_status spa2_mask_workspace_size(const spa2_desc* desc, size_t* bytes);
+
+/* Steps 1-3: pool, P-bar, Top-k U Top-p, compacted row and column lists.
+ * k_frac, p_frac in [0, 1], not both 0. Per row, Top-k keeps the first
+ * n_k = min(T_n, ceil(k_frac * T_n - 1e-9)) blocks of the order (P-bar descending,
+ * block index ascending); Top-p keeps every block of that order whose exclusive prefix
+ * sum of P-bar is below p_frac (the smallest prefix that reaches p); the mask is their
+ * union (rainbus summary, "前置知识" for the Top-k / Top-p rules, "研究动机" for the
+ * worked rows, "技术新颖性" for the union). P-bar is computed in double precision.
+ * pbar_out: optional double [B, H, T_m, T_n] copy of P-bar (NULL = not written).
+ * workspace: device buffer of at least spa2_mask_workspace_size bytes. */
+spa2_status spa2_mask(const spa2_desc* desc, const void* q, const void* k, double k_frac,
+                      double p_frac, const spa2_blockmask* out, double* pbar_out,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Step 3 alone: the hybrid selection on a given P-bar (double [B, H, T_m, T_n], rows
+ * summing to 1) -> mask and lists. Same rule as spa2_mask. */
+spa2_status spa2_select(const spa2_desc* desc, const double* pbar, double k_frac,
+                        double p_frac, const spa2_blockmask* out, void* stream);
+
+/* Rebuild row and column lists from a caller-filled out->mask (for masks made outside
+ * this library). */
+spa2_status spa2_mask_lists(const spa2_desc* desc, const spa2_blockmask* m, void* stream);
+
+/* Step 4, forward (rainbus summary, "方法步骤详情", step 4): for every query row, the
+ * softmax of q.k/sqrt(D) over the keys of the kept key blocks, O = weights . V, and
+ * LSE. m = NULL runs dense attention (every block kept) through the same kernel.
+ * o: [B, H, N, D] dtype, lse: float [B, H, N].
+ * o_f32: optional float [B, H, N, D] copy of O before rounding to dtype (NULL = not
+ * written). Handing it to the backward lets the row term rowsum(dO * O) use the
+ * unrounded O; with bf16 and keys that share a large offset (attention sinks) the
+ * rounded O alone costs dQ several percent of accuracy. */
+spa2_status spa2_fwd(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                     const spa2_blockmask* m, void* o, float* lse, float* o_f32,
+                     void* stream);
+
+/* Workspace bytes that spa2_bwd needs (the per-row dot(dO, O) vector, float). */
+spa2_status spa2_bwd_workspace_size(const spa2_desc* desc, size_t* bytes);
+
+/* Backward of spa2_fwd with the same mask held fixed (the mask gets no gradient):
+ *   dP = dO V^T, dS = P * (dP - rowsum(dO * O)), dQ = dS K / sqrt(D),
+ *   dK = dS^T Q / sqrt(D), dV = P^T dO, over kept pairs only, with P rebuilt from LSE.
+ * o, lse (and o_f32 if not NULL) are the forward's outputs for the same inputs and mask;
+ * rowsum(dO * O) reads o_f32 when given, else o. m = NULL is dense.
+ * dq, dk, dv: [B, H, N, D] dtype (fully overwritten). Deterministic: every output
+ * element is reduced in a fixed order. */
+spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                     const void* o, const float* o_f32, const float* lse, const void* dout,
+                     const spa2_blockmask* m, void* dq, void* dk, void* dv, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+/* The three kernels of spa2_bwd, callable one by one (for example to run the dK/dV pass
+ * and the dQ pass on two streams once the preprocess has finished). spa2_bwd is exactly
+ * spa2_bwd_prep, then spa2_bwd_dkdv, then spa2_bwd_dq on one stream.
+ *   spa2_bwd_prep: dvec[B, H, N] (float, device) = rowsum(dO * O), O = o_f32 if given;
+ *   spa2_bwd_dkdv: dK, dV from the column lists (one workgroup per key block);
+ *   spa2_bwd_dq:   dQ from the row lists (one workgroup per query block).
+ * dvec must hold spa2_bwd_prep's result for the same O and dO. */
+spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f32,
+                          const void* dout, float* dvec, void* stream);
+spa2_status spa2_bwd_dkdv(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, const float* dvec,
+                          const spa2_blockmask* m, void* dk, void* dv, void* stream);
+spa2_status spa2_bwd_dq(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                        const float* lse, const void* dout, const float* dvec,
+                        const spa2_blockmask* m, void* dq, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA2_H */

@@ -187,8 +187,11 @@ def _kept_keys(n: int, bkv: int, cols) -> np.ndarray:
     return np.concatenate([np.arange(*block_range(n, bkv, j)) for j in cols])
 
 
-def attn_fwd_head(q, k, v, mask, bq: int, bkv: int):
-    """O [N, d], LSE [N] (natural log) for one head under block mask [T_m, T_n]."""
+def attn_fwd_head(q, k, v, mask, bq: int, bkv: int, rows=None):
+    """O [N, d], LSE [N] (natural log) for one head under block mask [T_m, T_n].
+
+    rows: optional iterable of query-block indices to compute (others stay O = 0,
+    LSE = -inf); each computed block is exact, so sampled checks stay exact."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -196,7 +199,7 @@ def attn_fwd_head(q, k, v, mask, bq: int, bkv: int):
     scale = 1.0 / math.sqrt(d)
     out = np.zeros((n, v.shape[1]), dtype=np.float64)
     lse = np.full(n, -np.inf, dtype=np.float64)
-    for i in range(mask.shape[0]):
+    for i in (range(mask.shape[0]) if rows is None else rows):
         lo, hi = block_range(n, bq, i)
         keys = _kept_keys(n, bkv, np.flatnonzero(mask[i]))
         if keys.size == 0:
@@ -228,8 +231,12 @@ def attn_fwd(q, k, v, mask, bq: int, bkv: int):
 #   dP = dO V_C^T,  dS = P * (dP - rowsum(P * dP)),
 #   dQ = dS K_C / sqrt(d),  dK_C += dS^T Q / sqrt(d),  dV_C += P^T dO.
 # ---------------------------------------------------------------------------------------
-def attn_bwd_head(q, k, v, do, mask, bq: int, bkv: int):
-    """dQ, dK, dV [N, d] for one head."""
+def attn_bwd_head(q, k, v, do, mask, bq: int, bkv: int, rows=None):
+    """dQ, dK, dV [N, d] for one head.
+
+    rows: optional iterable of query-block indices whose contributions are summed. dQ of a
+    listed block is complete; dK/dV of key block j are complete when every query block
+    that keeps j is listed."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -239,7 +246,7 @@ def attn_bwd_head(q, k, v, do, mask, bq: int, bkv: int):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for i in range(mask.shape[0]):
+    for i in (range(mask.shape[0]) if rows is None else rows):
         lo, hi = block_range(n, bq, i)
         keys = _kept_keys(n, bkv, np.flatnonzero(mask[i]))
         if keys.size == 0:

@@ -1,0 +1,150 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the header
+declares, and rejects every invalid argument with its status code before any HIP call
+(so no device is touched: the pointers passed here are never dereferenced)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_spa2_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spa2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libspa2.so not built (run __graft_entry__.build())")
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\*?(spa2_[a-z_]+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert {"spa2_mask", "spa2_fwd", "spa2_bwd", "spa2_select", "spa2_pool"} <= set(names)
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def good(**kw):
+    d = dict(B=1, H=2, N=1000, D=128, BQ=128, BKV=64, dtype=_lib.BF16)
+    d.update(kw)
+    return _lib.Desc(**d)
+
+
+def bm(**kw):
+    m = dict(mask=FAKE, row_cnt=FAKE, row_idx=FAKE, col_cnt=FAKE, col_idx=FAKE)
+    m.update(kw)
+    return _lib.BlockMaskC(**m)
+
+
+def mask_call(desc=None, q=FAKE, k=FAKE, kf=0.1, pf=0.5, out=None, ws=FAKE, wsb=1 << 40):
+    L = _lib.lib()
+    return L.spa2_mask(C.byref(desc or good()), q, k, kf, pf, C.byref(out or bm()), None, ws,
+                       wsb, None)
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for s in range(7):
+        assert L.spa2_status_str(s)
+    assert L.spa2_num_blocks(32760, 128) == 256 and L.spa2_num_blocks(75600, 64) == 1182
+    assert L.spa2_num_blocks(0, 64) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), _lib.E_SHAPE), (dict(N=(1 << 20) + 1), _lib.E_SHAPE), (dict(B=0), _lib.E_SHAPE),
+    (dict(H=-1), _lib.E_SHAPE), (dict(D=96), _lib.E_SHAPE), (dict(D=256), _lib.E_SHAPE),
+    (dict(BQ=32), _lib.E_SHAPE), (dict(BQ=256), _lib.E_SHAPE), (dict(BKV=128), _lib.E_SHAPE),
+    (dict(N=4096 * 64 + 1), _lib.E_SHAPE), (dict(dtype=7), _lib.E_DTYPE),
+])
+def test_bad_desc(kw, code):
+    assert mask_call(desc=good(**kw)) == code
+    L = _lib.lib()
+    d = good(**kw)
+    assert L.spa2_fwd(C.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None) == code
+    assert L.spa2_bwd(C.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE,
+                      FAKE, FAKE, 1 << 40, None) == code
+    assert L.spa2_bwd_prep(C.byref(d), FAKE, None, FAKE, FAKE, None) == code
+    assert L.spa2_bwd_dkdv(C.byref(d), *[FAKE] * 6, None, FAKE, FAKE, None) == code
+    assert L.spa2_bwd_dq(C.byref(d), *[FAKE] * 6, None, FAKE, None) == code
+    n = C.c_size_t(0)
+    assert L.spa2_mask_workspace_size(C.byref(d), C.byref(n)) == code
+
+
+@pytest.mark.parametrize("kf,pf", [(-0.1, 0.5), (1.5, 0.5), (0.1, -1e-9), (0.1, 1.0000001),
+                                   (float("nan"), 0.5), (0.1, float("nan")), (0.0, 0.0)])
+def test_bad_fractions(kf, pf):
+    assert mask_call(kf=kf, pf=pf) == _lib.E_PARAM
+    L = _lib.lib()
+    assert L.spa2_select(C.byref(good()), FAKE, kf, pf, C.byref(bm()), None) == _lib.E_PARAM
+
+
+def test_null_pointers():
+    L = _lib.lib()
+    assert mask_call(q=None) == _lib.E_NULL
+    assert mask_call(k=None) == _lib.E_NULL
+    for field in ("mask", "row_cnt", "row_idx", "col_cnt", "col_idx"):
+        assert mask_call(out=bm(**{field: None})) == _lib.E_NULL
+    assert L.spa2_mask(None, FAKE, FAKE, 0.1, 0.5, C.byref(bm()), None, FAKE, 1, None) == _lib.E_NULL
+    d = C.byref(good())
+    args = [FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None]  # q k v m o lse o_f32 stream
+    for i in (0, 1, 2, 4, 5):
+        a = list(args)
+        a[i] = None
+        assert L.spa2_fwd(d, *a) == _lib.E_NULL
+    # a mask without row lists
+    assert L.spa2_fwd(d, FAKE, FAKE, FAKE, C.byref(bm(row_idx=None)), FAKE, FAKE, None,
+                      None) == _lib.E_NULL
+    # q k v o o_f32 lse dout m dq dk dv ws ws_bytes stream
+    bargs = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 4 + [1 << 40, None]
+    for i in (0, 1, 2, 3, 5, 6, 8, 9, 10):
+        a = list(bargs)
+        a[i] = None
+        assert L.spa2_bwd(d, *a) == _lib.E_NULL, i
+    assert L.spa2_bwd(d, *bargs[:7], C.byref(bm(col_cnt=None)), *bargs[8:]) == _lib.E_NULL
+    # the staged backward: prep (o, o_f32, dout, dvec), dkdv, dq
+    assert L.spa2_bwd_prep(d, FAKE, None, None, FAKE, None) == _lib.E_NULL
+    assert L.spa2_bwd_prep(d, FAKE, None, FAKE, None, None) == _lib.E_NULL
+    st = [FAKE] * 6  # q k v lse dout dvec
+    for i in range(6):
+        a = list(st)
+        a[i] = None
+        assert L.spa2_bwd_dkdv(d, *a, None, FAKE, FAKE, None) == _lib.E_NULL
+        assert L.spa2_bwd_dq(d, *a, None, FAKE, None) == _lib.E_NULL
+    assert L.spa2_bwd_dkdv(d, *st, C.byref(bm(col_idx=None)), FAKE, FAKE, None) == _lib.E_NULL
+    assert L.spa2_bwd_dq(d, *st, C.byref(bm(row_cnt=None)), FAKE, None) == _lib.E_NULL
+    assert L.spa2_bwd_dq(d, *st, None, None, None) == _lib.E_NULL
+    assert L.spa2_pool(d, FAKE, None, FAKE, FAKE, None) == _lib.E_NULL
+    assert L.spa2_mask_lists(d, C.byref(bm(mask=None)), None) == _lib.E_NULL
+
+
+def test_workspace_checks():
+    L = _lib.lib()
+    d = good()
+    n = C.c_size_t(0)
+    assert L.spa2_mask_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
+    tm, tn = 8, 16
+    assert n.value == 2 * ((tm + tn) * 128 + tm * tn) * 8
+    assert mask_call(ws=None) == _lib.E_WORKSPACE
+    assert mask_call(wsb=n.value - 1) == _lib.E_WORKSPACE
+    assert L.spa2_bwd_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
+    assert n.value == 2 * 1000 * 4
+    head = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 3
+    assert L.spa2_bwd(C.byref(d), *head, FAKE, n.value - 1, None) == _lib.E_WORKSPACE
+    assert L.spa2_bwd(C.byref(d), *head, None, n.value, None) == _lib.E_WORKSPACE
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    """The Python layer has no fallback: a missing library is an import-time error."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.lib()

@@ -1,0 +1,81 @@
+"""Parity at the full Wan-shaped sizes, in the launch configuration the benchmark times
+(same entry points, same shapes, same calibrated k/p).
+
+Masks are compared for every head; O/LSE/dQ on sampled query blocks and dK/dV on sampled
+key blocks (the first key block is the sink that nearly every row keeps), which the
+oracle computes exactly block by block."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_spa2_amd as spa2
+import oracle
+from gen import configs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wan13b():
+    w = configs.params("wan13b_480p")
+    print(f"[wan13b_480p] drawing inputs, p={w['p']}", flush=True)
+    inp = configs.make_inputs("wan13b_480p")
+    mask, infos = gu.oracle_masks(inp, w["BQ"], w["BKV"], w["k"], w["p"])
+    dev = {x: gu.to_dev(getattr(inp, x)) for x in ("q", "k", "v", "do")}
+    return dict(w=w, inp=inp, mask=mask, infos=infos, dev=dev)
+
+
+def test_wan13b_mask_all_heads(wan13b):
+    w, d = wan13b["w"], wan13b["dev"]
+    bm = spa2.mask(d["q"], d["k"], w["k"], w["p"], w["BQ"], w["BKV"])
+    g = bm.mask.cpu().numpy().astype(bool)
+    cls = gu.classify_mask(g, wan13b["mask"], wan13b["infos"])
+    print(f"[wan13b_480p] kept {g.mean():.6f} (oracle {wan13b['mask'].mean():.6f}); {cls}")
+    assert cls["other"] == 0 and cls["k_band"] == 0, cls
+    assert abs(wan13b["mask"].mean() - 0.05) < 1e-4
+
+
+def test_wan13b_fwd_bwd_sampled(wan13b):
+    w, d, inp = wan13b["w"], wan13b["dev"], wan13b["inp"]
+    bq, bkv, N = w["BQ"], w["BKV"], w["N"]
+    bm = spa2.mask(d["q"], d["k"], w["k"], w["p"], bq, bkv)
+    gm = bm.mask.cpu().numpy().astype(bool)
+    of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
+    dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
+    on, ln = gu.to_f64(o), lse.cpu().numpy().astype(np.float64)
+    dqn, dkn, dvn = gu.to_f64(dq), gu.to_f64(dk), gu.to_f64(dv)
+    tm, tn = gm.shape[-2:]
+    rng = np.random.default_rng(0)
+    for h in range(w["H"]):
+        m = gm[0, h]
+        q, k, v, do = (inp.head_f64(x, 0, h) for x in ("q", "k", "v", "do"))
+        qblocks = sorted({0, tm - 1, int(rng.integers(tm))})
+        kblocks = sorted({tn - 1, int(rng.integers(1, tn - 1))} | ({0} if h < 2 else set()))
+        rows = sorted(set(qblocks) | {i for j in kblocks for i in np.flatnonzero(m[:, j])})
+        o_ref, lse_ref = oracle.attn_fwd_head(q, k, v, m, bq, bkv, rows=qblocks)
+        dq_ref, dk_ref, dv_ref = oracle.attn_bwd_head(q, k, v, do, m, bq, bkv, rows=rows)
+        qr = np.concatenate([np.arange(i * bq, min(N, (i + 1) * bq)) for i in qblocks])
+        kr = np.concatenate([np.arange(j * bkv, min(N, (j + 1) * bkv)) for j in kblocks])
+        gu.check_close(f"O h{h}", on[0, h][qr], o_ref[qr], "bf16")
+        gu.check_lse(ln[0, h][qr], lse_ref[qr], "bf16")
+        gu.check_close(f"dQ h{h}", dqn[0, h][qr], dq_ref[qr], "bf16")
+        gu.check_close(f"dK h{h}", dkn[0, h][kr], dk_ref[kr], "bf16")
+        gu.check_close(f"dV h{h}", dvn[0, h][kr], dv_ref[kr], "bf16")
+
+
+def test_staged_backward_equals_bwd(wan13b):
+    """spa2_bwd equals its three stages called one by one, bit for bit."""
+    w, d = wan13b["w"], wan13b["dev"]
+    bm = spa2.mask(d["q"], d["k"], w["k"], w["p"], w["BQ"], w["BKV"])
+    of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
+    g1 = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
+    dvec = torch.empty_like(lse)
+    spa2.bwd_prep(o, d["do"], dvec, o_f32=of)
+    dk, dv = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec, bm,
+                           torch.empty_like(o), torch.empty_like(o))
+    dq = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], dvec, bm, torch.empty_like(o))
+    for a, b in zip(g1, (dq, dk, dv)):
+        assert torch.equal(a, b)

@@ -1,0 +1,274 @@
+"""GPU parity: every stage of the HIP path against the float64 oracle, element by element,
+at sizes the oracle finishes in seconds that span several tiles and ragged tails.
+
+Bars: masks bit-exact except blocks whose exclusive prefix mass lies within 1e-6 of p
+(counted and printed); O/dQ/dK/dV within 2e-2 relative L2 (bf16) or 1e-4 max-abs (fp32);
+LSE within 1e-3 (bf16) / 1e-4 (fp32); pooled vectors exact (bf16) and P-bar within 1e-12
+relative, both double precision."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_spa2_amd as spa2
+import oracle
+from gen import configs, synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name):
+    if name == "tiny_fp32":
+        w = configs.params("tiny_fp32")
+        return configs.make_inputs("tiny_fp32"), w["BQ"], w["BKV"], w["k"], w["p"]
+    if name == "mid_bf16":
+        w = configs.params("mid_bf16")
+        return configs.make_inputs("mid_bf16"), w["BQ"], w["BKV"], w["k"], w["p"]
+    spec = {
+        # name: (B, H, N, D, BQ, dtype, seed, k, p)
+        "ragged_bf16": (2, 2, 1000, 128, 128, "bf16", 11, 0.10, 0.50),
+        "ragged_bf16_d64": (1, 3, 777, 64, 64, "bf16", 12, 0.15, 0.40),
+        "ragged_f32_d128": (1, 2, 600, 128, 128, "f32", 13, 0.20, 0.50),
+        "ragged_f32_d64_bq128": (1, 2, 700, 64, 128, "f32", 14, 0.20, 0.30),
+        "single_block": (1, 2, 50, 64, 64, "bf16", 15, 0.50, 0.50),
+        "one_row": (1, 1, 1, 128, 128, "bf16", 16, 0.50, 0.50),
+    }[name]
+    B, H, N, D, BQ, dt, seed, k, p = spec
+    return synth.sink_inputs(B, H, N, D, 64, seed=seed, dtype=dt), BQ, 64, k, p
+
+
+CASES = ["tiny_fp32", "ragged_bf16", "ragged_bf16_d64", "ragged_f32_d128",
+         "ragged_f32_d64_bq128", "single_block", "one_row", "mid_bf16"]
+_CACHE = {}
+
+
+def ref(name):
+    """Inputs, device tensors and oracle results for a case (cached per session)."""
+    if name not in _CACHE:
+        inp, bq, bkv, k, p = _case(name)
+        print(f"[case {name}] shape={inp.q.shape} dtype={inp.dtype} bq={bq} k={k} p={p}",
+              flush=True)
+        mask, infos = gu.oracle_masks(inp, bq, bkv, k, p)
+        q, kk, v, do = (inp.f64(x) for x in ("q", "k", "v", "do"))
+        o, lse = oracle.attn_fwd(q, kk, v, mask, bq, bkv)
+        dq, dk, dv = oracle.attn_bwd(q, kk, v, do, mask, bq, bkv)
+        dev = {x: gu.to_dev(getattr(inp, x)) for x in ("q", "k", "v", "do")}
+        _CACHE[name] = dict(inp=inp, bq=bq, bkv=bkv, k=k, p=p, mask=mask, infos=infos, o=o,
+                            lse=lse, dq=dq, dk=dk, dv=dv, dev=dev)
+    return _CACHE[name]
+
+
+def _oracle_bm(r):
+    return spa2.mask_lists(torch.from_numpy(r["mask"].astype(np.uint8)).cuda(), r["dev"]["q"],
+                           r["bq"], r["bkv"])
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_pool(name):
+    r = ref(name)
+    qbar, kbar = spa2.pool(r["dev"]["q"], r["dev"]["k"], r["bq"], r["bkv"])
+    B, H = r["inp"].q.shape[:2]
+    gq = qbar.cpu().numpy().reshape(B * H, *qbar.shape[2:])
+    gk = kbar.cpu().numpy().reshape(B * H, *kbar.shape[2:])
+    for hh, info in enumerate(r["infos"]):
+        if r["inp"].dtype == "bf16":  # block sums of bf16 values are exact in double
+            assert np.array_equal(gq[hh], info["qbar"]) and np.array_equal(gk[hh], info["kbar"])
+        else:
+            np.testing.assert_allclose(gq[hh], info["qbar"], rtol=1e-15, atol=1e-16)
+            np.testing.assert_allclose(gk[hh], info["kbar"], rtol=1e-15, atol=1e-16)
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_pbar_and_mask(name):
+    r = ref(name)
+    bm, pbar = spa2.mask(r["dev"]["q"], r["dev"]["k"], r["k"], r["p"], r["bq"], r["bkv"],
+                         return_pbar=True)
+    torch.cuda.synchronize()
+    B, H = r["inp"].q.shape[:2]
+    gp = pbar.cpu().numpy().reshape(B * H, *pbar.shape[2:])
+    for hh, info in enumerate(r["infos"]):
+        np.testing.assert_allclose(gp[hh], info["pbar"], rtol=1e-12, atol=1e-300)
+    gmask = bm.mask.cpu().numpy().astype(bool)
+    cls = gu.classify_mask(gmask, r["mask"], r["infos"])
+    print(f"[{name}] mask mismatches: {cls}")
+    assert cls["other"] == 0 and cls["k_band"] == 0, cls
+    # lists are the ascending compaction of the mask the kernel produced
+    row_cnt, col_cnt = gu.lists_from_mask(gmask)
+    assert np.array_equal(bm.row_cnt.cpu().numpy(), row_cnt)
+    assert np.array_equal(bm.col_cnt.cpu().numpy(), col_cnt)
+    ri, ci = bm.row_idx.cpu().numpy(), bm.col_idx.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            for i in range(gmask.shape[2]):
+                assert list(ri[b, h, i, :row_cnt[b, h, i]]) == list(np.flatnonzero(gmask[b, h, i]))
+            for j in range(gmask.shape[3]):
+                assert list(ci[b, h, j, :col_cnt[b, h, j]]) == list(np.flatnonzero(gmask[b, h, :, j]))
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_select_on_oracle_pbar(name):
+    """The selection kernel alone, fed the oracle's own P-bar: the same values on both
+    sides, so only the prefix-sum order can differ (p-band)."""
+    r = ref(name)
+    B, H = r["inp"].q.shape[:2]
+    pb = np.stack([info["pbar"] for info in r["infos"]]).reshape(B, H, *r["mask"].shape[2:])
+    bm = spa2.select(torch.from_numpy(pb).cuda(), r["k"], r["p"], r["dev"]["q"], r["bq"], r["bkv"])
+    cls = gu.classify_mask(bm.mask.cpu().numpy().astype(bool), r["mask"], r["infos"])
+    assert cls["other"] == 0 and cls["k_band"] == 0, cls
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_fwd(name):
+    r = ref(name)
+    bm = _oracle_bm(r)
+    o, lse = spa2.fwd(r["dev"]["q"], r["dev"]["k"], r["dev"]["v"], bm)
+    st = gu.check_close("O", gu.to_f64(o), r["o"], r["inp"].dtype)
+    e = gu.check_lse(lse.cpu().numpy().astype(np.float64), r["lse"], r["inp"].dtype)
+    print(f"[{name}] fwd O {st} LSE {e:.2e}")
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_bwd(name):
+    r = ref(name)
+    d = r["dev"]
+    bm = _oracle_bm(r)
+    of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
+    dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
+    out = {}
+    for nm, got, want in (("dQ", dq, r["dq"]), ("dK", dk, r["dk"]), ("dV", dv, r["dv"])):
+        out[nm] = gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
+    print(f"[{name}] bwd {out}")
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_f32_d64_bq128"])
+def test_end_to_end_mask_fwd_bwd(name):
+    """GPU mask -> GPU forward -> GPU backward, compared with the oracle's whole chain."""
+    r = ref(name)
+    d = r["dev"]
+    bm = spa2.mask(d["q"], d["k"], r["k"], r["p"], r["bq"], r["bkv"])
+    assert np.array_equal(bm.mask.cpu().numpy().astype(bool), r["mask"])
+    of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
+    dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
+    gu.check_close("O", gu.to_f64(o), r["o"], r["inp"].dtype)
+    for nm, got, want in (("dQ", dq, r["dq"]), ("dK", dk, r["dk"]), ("dV", dv, r["dv"])):
+        gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_bf16_d64"])
+def test_dense_path(name):
+    """mask = NULL runs every block; it equals the all-ones mask bit for bit and the
+    oracle's dense attention."""
+    r = ref(name)
+    d = r["dev"]
+    B, H, N, D = r["inp"].q.shape
+    ones = torch.ones((B, H, spa2.num_blocks(N, r["bq"]), spa2.num_blocks(N, r["bkv"])),
+                      dtype=torch.uint8, device="cuda")
+    full = spa2.mask_lists(ones, d["q"], r["bq"], r["bkv"])
+    o1, l1 = spa2.fwd(d["q"], d["k"], d["v"], None, r["bq"], r["bkv"])
+    o2, l2 = spa2.fwd(d["q"], d["k"], d["v"], full)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = spa2.bwd(d["q"], d["k"], d["v"], o1, l1, d["do"], None, r["bq"], r["bkv"])
+    g2 = spa2.bwd(d["q"], d["k"], d["v"], o2, l2, d["do"], full)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    q, k, v, do = (r["inp"].f64(x) for x in ("q", "k", "v", "do"))
+    allm = np.ones((B, H) + tuple(ones.shape[2:]), dtype=bool)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, allm, r["bq"], r["bkv"])
+    gu.check_close("O dense", gu.to_f64(o1), o_ref, r["inp"].dtype)
+    gu.check_lse(l1.cpu().numpy().astype(np.float64), lse_ref, r["inp"].dtype)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, allm, r["bq"], r["bkv"])
+    for nm, got, want in (("dQ", g1[0], dq), ("dK", g1[1], dk), ("dV", g1[2], dv)):
+        gu.check_close(nm + " dense", gu.to_f64(got), want, r["inp"].dtype)
+
+
+@pytest.mark.parametrize("kf,pf", [(1.0, 0.0), (0.0, 1.0), (0.0, 0.3), (0.3, 0.0), (0.01, 0.9),
+                                   (1e-12, 0.2)])
+def test_mask_extremes(kf, pf):
+    """Top-k only, Top-p only, everything kept, and tiny k (n_k = 0)."""
+    inp = synth.sink_inputs(1, 2, 1000, 128, 64, seed=21, dtype="bf16")
+    mask, infos = gu.oracle_masks(inp, 128, 64, kf, pf)
+    bm = spa2.mask(gu.to_dev(inp.q), gu.to_dev(inp.k), kf, pf, 128, 64)
+    cls = gu.classify_mask(bm.mask.cpu().numpy().astype(bool), mask, infos)
+    assert cls["other"] == 0 and cls["k_band"] == 0, cls
+    if kf == 1.0 or pf == 1.0:
+        assert bm.mask.cpu().numpy().all() or cls["p_band"] > 0
+
+
+def test_empty_rows():
+    """A query block that keeps nothing gets O = 0, LSE = -inf, dQ = 0; the other blocks are
+    unaffected."""
+    r = ref("ragged_bf16")
+    d = r["dev"]
+    m = r["mask"].copy()
+    m[0, 1, 3] = False
+    m[1, 0, 7] = False  # the partial tail block
+    bm = spa2.mask_lists(torch.from_numpy(m.astype(np.uint8)).cuda(), d["q"], r["bq"], r["bkv"])
+    assert int(bm.row_cnt[0, 1, 3]) == 0
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm)
+    dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm)
+    q, k, v, do = (r["inp"].f64(x) for x in ("q", "k", "v", "do"))
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, m, r["bq"], r["bkv"])
+    refs = oracle.attn_bwd(q, k, v, do, m, r["bq"], r["bkv"])
+    on, ln = gu.to_f64(o), lse.cpu().numpy().astype(np.float64)
+    assert np.all(on[0, 1, 384:512] == 0) and np.all(np.isneginf(ln[0, 1, 384:512]))
+    assert np.all(gu.to_f64(dq)[0, 1, 384:512] == 0)
+    gu.check_close("O", on, o_ref, "bf16")
+    gu.check_lse(ln, lse_ref, "bf16")
+    for nm, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+        gu.check_close(nm, gu.to_f64(got), want, "bf16")
+
+
+def test_deterministic_and_in_bounds():
+    """Two runs are bitwise identical, and nothing is written past the outputs (guard
+    regions after each output stay intact; NaN-prefilled outputs are fully overwritten)."""
+    r = ref("ragged_bf16")
+    d = r["dev"]
+    B, H, N, D = r["inp"].q.shape
+    guard = 4096
+
+    def guarded(shape, dtype, fill):
+        n = int(np.prod(shape))
+        flat = torch.full((n + guard,), fill, dtype=dtype, device="cuda")
+        return flat, flat[:n].view(shape)
+
+    outs = []
+    for _ in range(2):
+        bm = spa2.mask(d["q"], d["k"], r["k"], r["p"], r["bq"], r["bkv"])
+        of, o = guarded((B, H, N, D), torch.bfloat16, float("nan"))
+        lf, lse = guarded((B, H, N), torch.float32, float("nan"))
+        spa2.fwd(d["q"], d["k"], d["v"], bm, out=(o, lse))
+        grads = [guarded((B, H, N, D), torch.bfloat16, float("nan")) for _ in range(3)]
+        spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm,
+                 out=tuple(x[1] for x in grads))
+        torch.cuda.synchronize()
+        for flat, view in [(of, o), (lf, lse)] + grads:
+            assert torch.isnan(flat[view.numel():]).all(), "write past the end of an output"
+            assert not torch.isnan(view).any(), "output not fully written"
+        outs.append([bm.mask.clone(), bm.row_cnt.clone(), bm.col_cnt.clone(), o.clone(),
+                     lse.clone()] + [x[1].clone() for x in grads])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "mid_bf16"])
+def test_bwd_without_unrounded_o(name):
+    """The backward also accepts only the rounded O (row term from bf16 O)."""
+    r = ref(name)
+    d = r["dev"]
+    bm = _oracle_bm(r)
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm)
+    dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm)
+    for nm, got, want in (("dQ", dq, r["dq"]), ("dK", dk, r["dk"]), ("dV", dv, r["dv"])):
+        gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
+
+
+def test_o_f32_is_unrounded_o():
+    """o_f32 rounds (to nearest even) to exactly the O written in the input dtype."""
+    r = ref("ragged_bf16")
+    d = r["dev"]
+    of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    o, _ = spa2.fwd(d["q"], d["k"], d["v"], _oracle_bm(r), o_f32=of)
+    assert torch.equal(of.to(torch.bfloat16), o)
+    gu.check_close("O f32", of.cpu().numpy().astype(np.float64), r["o"], "bf16")
