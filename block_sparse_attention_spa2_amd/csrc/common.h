@@ -35,15 +35,60 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Max over the four lanes that share (l % 16): lanes l, l^16, l^32, l^48.
-__device__ __forceinline__ float max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// Cross-lane exchange without LDS: v_permlane16_swap / v_permlane32_swap applied to two
+// copies of x leave, in every lane l, the values of lanes {l, l^16} (resp. {l, l^32}).
+__device__ __forceinline__ float xchg16(float x, bool take_max) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float a = __builtin_bit_cast(float, (unsigned)r[0]);
+  const float b = __builtin_bit_cast(float, (unsigned)r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
 }
-__device__ __forceinline__ float sum4(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+__device__ __forceinline__ float xchg32(float x, bool take_max) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float a = __builtin_bit_cast(float, (unsigned)r[0]);
+  const float b = __builtin_bit_cast(float, (unsigned)r[1]);
+  return take_max ? fmaxf(a, b) : a + b;
 }
+// Max / sum over the four lanes that share (l % 16): lanes l, l^16, l^32, l^48.
+__device__ __forceinline__ float max4(float x) { return xchg32(xchg16(x, true), true); }
+__device__ __forceinline__ float sum4(float x) { return xchg32(xchg16(x, false), false); }
+
+// Work item for workgroup `bid` of `items`: consecutive items go to the same XCD
+// (workgroups are dispatched round-robin over the 8 XCDs), so the query blocks of one
+// head share that XCD's L2 for their K/V tiles.
+__device__ __forceinline__ int xcd_item(int bid, int items) {
+  const int q = items >> 3, r = items & 7, x = bid & 7, slot = bid >> 3;
+  return x * q + min(x, r) + slot;
+}
+
+// A block list read 64 entries at a time into one VGPR (entry i in lane i % 64), so the
+// index of block t is a v_readlane instead of a memory load inside the main loop.
+struct ListCursor {
+  const int32_t* list;
+  int cnt;
+  int held;  // entries [base, base + 64) of the list, one per lane
+  int base;
+  __device__ __forceinline__ void init(const int32_t* l_, int cnt_) {
+    list = l_;
+    cnt = cnt_;
+    base = 0;
+    held = lane_id() < cnt ? list[lane_id()] : 0;
+  }
+  // t must be wave-uniform and visited in increasing order
+  __device__ __forceinline__ int at(int t) {
+    if (t - base >= 64) {
+      base += 64;
+      held = base + lane_id() < cnt ? list[base + lane_id()] : 0;
+    }
+    return __builtin_amdgcn_readlane(held, t - base);
+  }
+};
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained): this wave's outstanding
+// vector memory operations, including direct-to-LDS loads, have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0xF70); }
 
 // ------------------------------------------------------------------------------------
 // Element traits: fragment type, MFMA step, conversions.
@@ -133,6 +178,57 @@ struct Tile {
   __device__ static __forceinline__ void store_chunk(char* base, int row, int chunk, u32x4 v) {
     *reinterpret_cast<u32x4*>(base + row * kRowBytes + ((chunk ^ swz(row)) << 4)) = v;
   }
+  // Fill the tile straight from global memory (global_load_lds, 16 bytes per lane) with
+  // rows row0 .. row0 + ROWS - 1 of a row-major [nrows, D] matrix; rows past nrows - 1 are
+  // clamped to the last row (finite data that the callers mask or weight by zero). Every
+  // wave of the workgroup (nwaves of them) issues kChunks * ROWS / (64 * nwaves) loads;
+  // lane l of a load lands at its 16-byte slot, so the swizzle is applied to the source
+  // address. Completion: wait_vmem() in each wave, then a workgroup barrier.
+  __device__ static __forceinline__ void load_async(char* base, const T* src, int row0, int nrows,
+                                                    int wave, int nwaves) {
+    constexpr int kPerWave = kChunks * ROWS / 64;  // 16-byte loads per wave if one wave
+    const int l = lane_id();
+    for (int i = wave; i < kPerWave; i += nwaves) {
+      const int f = i * 64 + l;  // flat 16-byte slot in the tile
+      const int row = f / kChunks, pc = f % kChunks;
+      const int grow = min(row0 + row, nrows - 1);
+      const T* g = src + (size_t)grow * D + ((pc ^ swz(row)) * (16 / (int)sizeof(T)));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                       (SPA2_LDS void*)(base + i * 1024), 16, 0, 0);
+    }
+  }
+
+  // The same fill for NW waves with the lane part of the source offsets computed once:
+  // off[n] = element offset of this lane's slot for load n (wave-relative) within a
+  // whole tile of ROWS valid rows.
+  template <int NW>
+  struct Plan {
+    static constexpr int kLoads = kChunks * ROWS / 64 / NW;  // loads per wave per tile
+    int off[kLoads];
+    __device__ __forceinline__ void init(int wave) {
+      const int l = lane_id();
+#pragma unroll
+      for (int n = 0; n < kLoads; ++n) {
+        const int f = (n * NW + wave) * 64 + l;
+        const int row = f / kChunks, pc = f % kChunks;
+        off[n] = row * D + (pc ^ swz(row)) * (16 / (int)sizeof(T));
+      }
+    }
+    // rows row0 .. row0 + ROWS - 1 all exist
+    __device__ __forceinline__ void issue(char* base, const T* src, int row0, int wave) const {
+      const T* tile = src + (size_t)row0 * D;
+#pragma unroll
+      for (int n = 0; n < kLoads; ++n)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + off[n]),
+                                         (SPA2_LDS void*)(base + (n * NW + wave) * 1024), 16, 0, 0);
+    }
+    // general case: rows past nrows - 1 clamped
+    __device__ __forceinline__ void issue_any(char* base, const T* src, int row0, int nrows,
+                                              int wave) const {
+      if (row0 + ROWS <= nrows) issue(base, src, row0, wave);
+      else load_async(base, src, row0, nrows, wave, NW);
+    }
+  };
   // 8 consecutive elements [col, col+8) of one row (col multiple of 8)
   __device__ static __forceinline__ typename Elem<T>::frag read_row8(const char* base, int row, int col);
   // 4 elements down column `col`, rows r0 .. r0+3 (the transposed operand half)

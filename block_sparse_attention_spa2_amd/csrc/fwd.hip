@@ -6,13 +6,17 @@
 // accumulates P_ij V_j. Masked pairs are skipped entirely: their K/V tiles are never
 // fetched.
 //
-// One workgroup (4 waves) per query block. Wave w owns BQ/4 query rows. Per kept key
-// block the workgroup stages K_j and V_j (64 x D) into a double-buffered, swizzled LDS
-// tile while the previous block is being computed. Scores are computed transposed,
-// S^T = K Q^T (operand A = K rows from LDS, operand B = Q held in registers), so each
-// lane owns one query column and the online-softmax state is lane local (the row max
-// needs the 4 lanes that share the column). P^T leaves the accumulators directly as the
+// One workgroup (4 waves) per query block; two workgroups share a CU (2 waves per SIMD,
+// so one wave's softmax overlaps the other's matrix work). Wave w owns BQ/4 query rows.
+// K_j and V_j (64 x D) stream from global memory straight into a double-buffered,
+// swizzled LDS tile (global_load_lds), issued one block ahead, with one barrier per
+// block. Scores are computed transposed, S^T = K Q^T (operand A = K rows from LDS,
+// operand B = Q held in registers), so each lane owns one query column and the
+// online-softmax state is lane local (the row max needs the 4 lanes that share the
+// column, combined with VALU lane swaps). P^T leaves the accumulators directly as the
 // B operand of O^T = V^T P^T; V^T comes from row-major LDS through transpose reads.
+// The running max is only raised (and O rescaled) when a row's block max exceeds it by
+// more than 2^8, so most blocks skip the rescale; the final normalisation is exact.
 #include <math.h>
 
 #include "common.h"
@@ -29,12 +33,15 @@ struct FwdArgs {
   float* o_f32;  // optional unrounded copy of O
   const int32_t* row_cnt;  // nullptr: dense
   const int32_t* row_idx;
-  int N, Tm, Tn;
+  int N, Tm, Tn, items;
   float scale_log2;  // log2(e) / sqrt(D)
 };
 
+// Rescale threshold in log2 units: probabilities stay below 2^8 between rescales.
+constexpr float kRescaleSlack = 8.0f;
+
 template <typename T, int D, int BQ>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BKV = 64;
@@ -42,18 +49,35 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 32;   // reduction steps over the head dimension
   constexpr int DT = D / 16;   // 16-wide output column tiles
   using KV = Tile<T, BKV, D>;
-  constexpr int CPR = KV::kChunks;       // 16-byte chunks per K/V row
-  constexpr int CH = BKV * CPR / 256;    // chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) char smem[2][2][KV::kBytes];
+  // Two stages in two separate LDS variables: every access names one of them statically
+  // (the loop below is unrolled by two), so the compiler can tell that the loads into one
+  // stage do not alias the reads of the other and does not wait for them early.
+  __shared__ __attribute__((aligned(1024))) char stage0[2 * KV::kBytes];
+  __shared__ __attribute__((aligned(1024))) char stage1[2 * KV::kBytes];
 
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, g = l >> 4, c16 = l & 15;
-  const int bh = blockIdx.x / a.Tm, qb = blockIdx.x % a.Tm;
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int item = xcd_item(blockIdx.x, a.items);
+  const int bh = item / a.Tm, qb = item % a.Tm;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const T* Q = (const T*)a.q + head;
   const T* K = (const T*)a.k + head;
   const T* V = (const T*)a.v + head;
   const int q0 = qb * BQ + w * 16 * QT;
+
+  const bool dense = a.row_cnt == nullptr;
+  const int cnt = dense ? a.Tn : a.row_cnt[item];
+  ListCursor cur;
+  if (!dense) cur.init(a.row_idx + (size_t)item * a.Tn, cnt);
+  auto block_of = [&](int t) { return dense ? t : cur.at(t); };
+  typename KV::template Plan<4> plan;
+  plan.init(w);
+  auto issue = [&](char* stage, int j) {
+    plan.issue_any(stage, K, j * BKV, N, w);
+    plan.issue_any(stage + KV::kBytes, V, j * BKV, N, w);
+  };
+  if (cnt > 0) issue(stage0, block_of(0));
 
   // Q as the B operand: lane -> query q0 + 16 qt + c16, dims 32 ks + 8 g .. +8
   F qf[QT][KS];
@@ -64,34 +88,6 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     for (int ks = 0; ks < KS; ++ks)
       qf[qt][ks] = row < N ? load_row8<T>(Q + (size_t)row * D + ks * 32 + 8 * g) : E::zero();
   }
-
-  const bool dense = a.row_cnt == nullptr;
-  const int cnt = dense ? a.Tn : a.row_cnt[blockIdx.x];
-  const int32_t* list = dense ? nullptr : a.row_idx + (size_t)blockIdx.x * a.Tn;
-
-  u32x4 kr[CH], vr[CH];
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
-      const int key = j * BKV + row;
-      if (key < N) {
-        kr[c] = *reinterpret_cast<const u32x4*>(K + (size_t)key * D + ch * (16 / sizeof(T)));
-        vr[c] = *reinterpret_cast<const u32x4*>(V + (size_t)key * D + ch * (16 / sizeof(T)));
-      } else {
-        kr[c] = u32x4{0, 0, 0, 0};
-        vr[c] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
-      KV::store_chunk(smem[buf][0], row, ch, kr[c]);
-      KV::store_chunk(smem[buf][1], row, ch, vr[c]);
-    }
-  };
 
   f32x4 oacc[DT][QT];
 #pragma unroll
@@ -105,18 +101,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     lrow[qt] = 0.f;
   }
 
-  if (cnt > 0) {
-    gload(dense ? 0 : list[0]);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < cnt; ++t) {
-    const int j = dense ? t : list[t];
-    const int buf = t & 1;
-    if (t + 1 < cnt) gload(dense ? t + 1 : list[t + 1]);
-    const char* Kb = smem[buf][0];
-    const char* Vb = smem[buf][1];
+  auto block = [&](int t, const char* stage, char* next) {
+    const int j = block_of(t);
+    const int jn = t + 1 < cnt ? block_of(t + 1) : 0;
+    wait_vmem();      // this wave's loads of block t have landed
+    __syncthreads();  // ... and every other wave's; block t-1 is no longer being read
+    if (t + 1 < cnt) issue(next, jn);
+    const char* Kb = stage;
+    const char* Vb = stage + KV::kBytes;
 
     // S^T = K Q^T : s[kt][qt] lane holds S^T[key 16 kt + 4 g + e][query 16 qt + c16]
     f32x4 s[4][QT];
@@ -145,30 +137,41 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     }
 
     // online softmax, per query column (base-2 exponent with the scale folded in)
+    float mx[QT];
+    bool raise = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float mx = -INFINITY;
+      float m = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
+        m = fmaxf(m, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
+      mx[qt] = max4(m) * a.scale_log2;
+      raise |= mx[qt] > mrow[qt] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: some row needs a new max
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[kt][qt][e]);
-      mx = max4(mx) * a.scale_log2;
-      const float mnew = fmaxf(mrow[qt], mx);
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mref);
-      mrow[qt] = mnew;
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mnew = fmaxf(mrow[qt], mx[qt]);
+        const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mnew);  // 0 on the first block
+        mrow[qt] = mnew;
+        lrow[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float mref = mrow[qt] == -INFINITY ? 0.f : mrow[qt];
       float ls = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[kt][qt][e] * a.scale_log2 - mref);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][e], a.scale_log2, -mref));
           s[kt][qt][e] = p;
           ls += p;
         }
-      lrow[qt] = lrow[qt] * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+      lrow[qt] += ls;
     }
 
     // O^T += V^T P^T over the block's 64 keys, 32 at a time
@@ -186,9 +189,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = E::mma(va, pf[qt], oacc[dt][qt]);
       }
     }
-
-    if (t + 1 < cnt) lstore(buf ^ 1);
-    __syncthreads();
+  };
+  for (int t = 0; t < cnt; t += 2) {
+    block(t, stage0, stage1);
+    if (t + 1 < cnt) block(t + 1, stage1, stage0);
   }
 
   // epilogue: normalise, store O rows and LSE
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const int32_t* row_cnt, const int32_t* row_idx, void* o, float* lse,
                       float* o_f32, hipStream_t st) {
-  FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, s.N, s.Tm, s.Tn,
+  FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, s.N, s.Tm, s.Tn, s.BH() * s.Tm,
             (float)(1.4426950408889634 / sqrt((double)s.D))};
   const dim3 grid(s.BH() * s.Tm);
 #define SPA2_FWD(T, D, BQ) fwd_kernel<T, D, BQ><<<grid, 256, 0, st>>>(a)
