@@ -86,12 +86,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   using KV = Tile<T, BKV, D>;
-  constexpr int CPR = KV::kChunks;
-  constexpr int CH = BKV * CPR / 256;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][KV::kBytes];
+  // two stages in two LDS variables, named statically (see the forward kernel)
+  __shared__ __attribute__((aligned(1024))) char stage0[2 * KV::kBytes];
+  __shared__ __attribute__((aligned(1024))) char stage1[2 * KV::kBytes];
 
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, g = l >> 4, c16 = l & 15;
-  const int bh = blockIdx.x / a.Tm, qb = blockIdx.x % a.Tm;
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int item = xcd_item(blockIdx.x, a.BH * a.Tm);
+  const int bh = item / a.Tm, qb = item % a.Tm;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const T* Q = (const T*)a.q + head;
@@ -99,6 +101,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const T* V = (const T*)a.v + head;
   const T* dO = (const T*)a.dout + head;
   const int q0 = qb * BQ + w * 16 * QT;
+
+  const bool dense = a.row_cnt == nullptr;
+  const int cnt = dense ? a.Tn : a.row_cnt[item];
+  ListCursor cur;
+  if (!dense) cur.init(a.row_idx + (size_t)item * a.Tn, cnt);
+  auto block_of = [&](int t) { return dense ? t : cur.at(t); };
+  typename KV::template Plan<4> plan;
+  plan.init(w);
+  auto issue = [&](char* stage, int j) {
+    plan.issue_any(stage, K, j * BKV, N, w);
+    plan.issue_any(stage + KV::kBytes, V, j * BKV, N, w);
+  };
+  if (cnt > 0) issue(stage0, block_of(0));
 
   F qf[QT][KS], df[QT][KS];
   float lse2[QT], dv[QT];
@@ -115,34 +130,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     dv[qt] = ok ? a.dvec[(size_t)bh * N + row] : 0.f;
   }
 
-  const bool dense = a.row_cnt == nullptr;
-  const int cnt = dense ? a.Tn : a.row_cnt[blockIdx.x];
-  const int32_t* list = dense ? nullptr : a.row_idx + (size_t)blockIdx.x * a.Tn;
-
-  u32x4 kr[CH], vr[CH];
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
-      const int key = j * BKV + row;
-      if (key < N) {
-        kr[c] = *reinterpret_cast<const u32x4*>(K + (size_t)key * D + ch * (16 / sizeof(T)));
-        vr[c] = *reinterpret_cast<const u32x4*>(V + (size_t)key * D + ch * (16 / sizeof(T)));
-      } else {
-        kr[c] = u32x4{0, 0, 0, 0};
-        vr[c] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
-      KV::store_chunk(smem[buf][0], row, ch, kr[c]);
-      KV::store_chunk(smem[buf][1], row, ch, vr[c]);
-    }
-  };
-
   // bf16 only: rounding corrections (see below). pkc accumulates sum_j P^blk_j c_j, the
   // attention-weighted block centres; tpart the lane's share of sum_k dS_k.
   constexpr bool kCorr = sizeof(T) == 2;
@@ -158,18 +145,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (cnt > 0) {
-    gload(dense ? 0 : list[0]);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < cnt; ++t) {
-    const int j = dense ? t : list[t];
-    const int buf = t & 1;
-    if (t + 1 < cnt) gload(dense ? t + 1 : list[t + 1]);
-    const char* Kb = smem[buf][0];
-    const char* Vb = smem[buf][1];
+  auto block = [&](int t, const char* stage, char* next) {
+    const int j = block_of(t);
+    const int jn = t + 1 < cnt ? block_of(t + 1) : 0;
+    wait_vmem();      // this wave's loads of block t have landed
+    __syncthreads();  // ... and every other wave's; block t-1 is no longer being read
+    if (t + 1 < cnt) issue(next, jn);
+    const char* Kb = stage;
+    const char* Vb = stage + KV::kBytes;
 
     f32x4 s[4][QT], dp[4][QT];
 #pragma unroll
@@ -261,9 +244,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
           }
       }
     }
-
-    if (t + 1 < cnt) lstore(buf ^ 1);
-    __syncthreads();
+  };
+  for (int t = 0; t < cnt; t += 2) {
+    block(t, stage0, stage1);
+    if (t + 1 < cnt) block(t + 1, stage1, stage0);
   }
 
   if constexpr (kCorr) {
@@ -296,28 +280,36 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// dK, dV: per key block, over the query blocks that keep it.
+// dK, dV: per key block, over the query blocks that keep it (column lists).
+// Wave w owns key half kh = w % 2 (32 keys) and query half qh = w / 2 of every query
+// block, so each wave reads only its half of Q_i and dO_i from LDS (in both layouts),
+// which halves the LDS traffic per matrix instruction compared with 16 keys per wave
+// over all rows. Q_i and dO_i stream into LDS with global_load_lds, one block ahead;
+// LSE and Dv of the wave's rows are read straight from global memory.
 //   S = Q K^T, dP = dO V^T (A = Q, dO rows from LDS; B = K, V in registers),
 //   dS = P * (dP - Dv), dV^T += dO^T P, dK^T += Q^T dS (A via transpose reads).
+// At the end the two query halves' partial sums are added through LDS.
 // ------------------------------------------------------------------------------------
 template <typename T, int D, int BQ>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BKV = 64;
-  constexpr int MT = BQ / 16;  // 16-row query tiles in a query block
+  constexpr int MT = BQ / 32;  // 16-row query tiles per wave (half of the query block)
+  constexpr int KT = 2;        // 16-key tiles per wave (32 keys)
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   using QTile = Tile<T, BQ, D>;
-  constexpr int CPR = QTile::kChunks;
-  constexpr int CH = BQ * CPR / 256;
-  constexpr int kStage = 2 * QTile::kBytes + 2 * BQ * (int)sizeof(float);
-  // two stages when they fit in the 160 KB of LDS, else one (fp32, D = BQ = 128)
-  constexpr int NBUF = 2 * kStage <= 160 * 1024 ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) char smem[NBUF][kStage];
+  constexpr int kStage = 2 * QTile::kBytes;  // Q_i and dO_i
+  constexpr int NS = 2 * kStage <= 160 * 1024 ? 2 : 1;  // one stage only if two do not fit
+  __shared__ __attribute__((aligned(1024))) char stage0[kStage];
+  __shared__ __attribute__((aligned(1024))) char stage1[NS == 2 ? kStage : 16];
 
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, g = l >> 4, c16 = l & 15;
-  const int bh = blockIdx.x / a.Tn, kb = blockIdx.x % a.Tn;
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = w & 1, qh = w >> 1;
+  const int item = xcd_item(blockIdx.x, a.BH * a.Tn);
+  const int bh = item / a.Tn, kb = item % a.Tn;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const T* Q = (const T*)a.q + head;
@@ -326,145 +318,192 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const T* dO = (const T*)a.dout + head;
   const float* LSE = a.lse + (size_t)bh * N;
   const float* DV = a.dvec + (size_t)bh * N;
-  const int key = kb * BKV + w * 16 + c16;  // this lane's key (B operand column)
-
-  F kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = key < N ? load_row8<T>(K + (size_t)key * D + ks * 32 + 8 * g) : E::zero();
-    vf[ks] = key < N ? load_row8<T>(V + (size_t)key * D + ks * 32 + 8 * g) : E::zero();
-  }
+  const int k0 = kb * BKV + kh * 32;  // first key of this wave
+  const int qrow0 = qh * (BQ / 2);    // first query row of this wave within a query block
 
   const bool dense = a.col_cnt == nullptr;
-  const int cnt = dense ? a.Tm : a.col_cnt[blockIdx.x];
-  const int32_t* list = dense ? nullptr : a.col_idx + (size_t)blockIdx.x * a.Tm;
-
-  u32x4 qr[CH], dr[CH];
-  float lr = 0.f, dvr = 0.f;
-  auto gload = [&](int i) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
-      const int q = i * BQ + row;
-      if (q < N) {
-        qr[c] = *reinterpret_cast<const u32x4*>(Q + (size_t)q * D + ch * (16 / sizeof(T)));
-        dr[c] = *reinterpret_cast<const u32x4*>(dO + (size_t)q * D + ch * (16 / sizeof(T)));
-      } else {
-        qr[c] = u32x4{0, 0, 0, 0};
-        dr[c] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < BQ) {
-      const int q = i * BQ + tid;
-      lr = q < N ? LSE[q] * kLog2e : INFINITY;  // rows past N get P = 0
-      dvr = q < N ? DV[q] : 0.f;
-    }
+  const int cnt = dense ? a.Tm : a.col_cnt[item];
+  ListCursor cur;
+  if (!dense) cur.init(a.col_idx + (size_t)item * a.Tm, cnt);
+  auto block_of = [&](int t) { return dense ? t : cur.at(t); };
+  typename QTile::template Plan<4> plan;
+  plan.init(w);
+  auto issue = [&](char* stage, int i) {
+    plan.issue_any(stage, Q, i * BQ, N, w);
+    plan.issue_any(stage + QTile::kBytes, dO, i * BQ, N, w);
   };
-  auto lstore = [&](int buf) {
-    char* base = smem[buf];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int flat = tid + c * 256, row = flat / CPR, ch = flat % CPR;
-      QTile::store_chunk(base, row, ch, qr[c]);
-      QTile::store_chunk(base + QTile::kBytes, row, ch, dr[c]);
-    }
-    float* stats = reinterpret_cast<float*>(base + 2 * QTile::kBytes);
-    if (tid < BQ) {
-      stats[tid] = lr;
-      stats[BQ + tid] = dvr;
-    }
-  };
+  if (cnt > 0) issue(stage0, block_of(0));
 
-  f32x4 dk[DT], dv[DT];
+  // K, V as B operands: lane -> key k0 + 16 kt + c16, dims 32 ks + 8 g .. +8
+  F kf[KT][KS], vf[KT][KS];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < KT; ++kt) {
+    const int key = k0 + kt * 16 + c16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[kt][ks] = key < N ? load_row8<T>(K + (size_t)key * D + ks * 32 + 8 * g) : E::zero();
+      vf[kt][ks] = key < N ? load_row8<T>(V + (size_t)key * D + ks * 32 + 8 * g) : E::zero();
+    }
   }
 
-  if (cnt > 0) {
-    gload(dense ? 0 : list[0]);
-    lstore(0);
-  }
-  __syncthreads();
+  // accumulators, transposed: lane holds [dim 16 dt + 4 g + e][key 16 kt + c16]
+  f32x4 dk[DT][KT], dv[DT][KT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      dk[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-  for (int t = 0; t < cnt; ++t) {
-    const int buf = NBUF == 2 ? (t & 1) : 0;
-    if (t + 1 < cnt) gload(dense ? t + 1 : list[t + 1]);
-    const char* Qb = smem[buf];
-    const char* Db = Qb + QTile::kBytes;
-    const float* stats = reinterpret_cast<const float*>(Qb + 2 * QTile::kBytes);
-
-    // S[query 16 mt + 4 g + e][key c16], dP likewise
-    f32x4 s[MT], dp[MT];
+  auto compute = [&](int i, const char* stage) {
+    const char* Qb = stage;
+    const char* Db = stage + QTile::kBytes;
+    // this lane's rows of the statistics: queries i*BQ + qrow0 + 16 mt + 4 g + e
+    f32x4 l4[MT], d4[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = i * BQ + qrow0 + mt * 16 + 4 * g;
+      if (r + 3 < N && ((reinterpret_cast<uintptr_t>(LSE + r) | reinterpret_cast<uintptr_t>(DV + r)) & 15) == 0) {
+        l4[mt] = *reinterpret_cast<const f32x4*>(LSE + r);
+        d4[mt] = *reinterpret_cast<const f32x4*>(DV + r);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l4[mt][e] = r + e < N ? LSE[r + e] : INFINITY;  // rows past N get P = 0
+          d4[mt][e] = r + e < N ? DV[r + e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l4[mt][e] *= kLog2e;
     }
+    // S[query 16 mt + 4 g + e][key 16 kt + c16], dP likewise
+    f32x4 s[MT][KT], dp[MT][KT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        s[mt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[mt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const F qa = QTile::read_row8(Qb, mt * 16 + c16, ks * 32 + 8 * g);
-        const F da = QTile::read_row8(Db, mt * 16 + c16, ks * 32 + 8 * g);
-        s[mt] = E::mma(qa, kf[ks], s[mt]);
-        dp[mt] = E::mma(da, vf[ks], dp[mt]);
+        const F qa = QTile::read_row8(Qb, qrow0 + mt * 16 + c16, ks * 32 + 8 * g);
+        const F da = QTile::read_row8(Db, qrow0 + mt * 16 + c16, ks * 32 + 8 * g);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          s[mt][kt] = E::mma(qa, kf[kt][ks], s[mt][kt]);
+          dp[mt][kt] = E::mma(da, vf[kt][ks], dp[mt][kt]);
+        }
       }
     }
-    // P and dS (P kept in s, dS in dp)
+    // P (kept in s) and dS (kept in dp)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + mt * 16 + 4 * g);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + BQ + mt * 16 + 4 * g);
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[mt][e] * a.scale_log2 - l4[e]);
-        s[mt][e] = p;
-        dp[mt][e] = p * (dp[mt][e] - d4[e]);
-      }
-    }
-    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the block's queries, 32 at a time)
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][kt][e], a.scale_log2, -l4[mt][e]));
+          s[mt][kt][e] = p;
+          dp[mt][kt][e] = p * (dp[mt][kt][e] - d4[mt][e]);
+        }
+    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the wave's queries, 32 at a time)
 #pragma unroll
     for (int u = 0; u < MT / 2; ++u) {
-      const F pf = E::pack(s[2 * u], s[2 * u + 1]);
-      const F sf = E::pack(dp[2 * u], dp[2 * u + 1]);
+      F pf[KT], sf[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        pf[kt] = E::pack(s[2 * u][kt], s[2 * u + 1][kt]);
+        sf[kt] = E::pack(dp[2 * u][kt], dp[2 * u + 1][kt]);
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         F dot, qtr;
-        QTile::read_col4(Db, 32 * u, dt * 16, dot, 0);
-        QTile::read_col4(Db, 32 * u + 16, dt * 16, dot, 1);
-        QTile::read_col4(Qb, 32 * u, dt * 16, qtr, 0);
-        QTile::read_col4(Qb, 32 * u + 16, dt * 16, qtr, 1);
-        dv[dt] = E::mma(dot, pf, dv[dt]);
-        dk[dt] = E::mma(qtr, sf, dk[dt]);
+        QTile::read_col4(Db, qrow0 + 32 * u, dt * 16, dot, 0);
+        QTile::read_col4(Db, qrow0 + 32 * u + 16, dt * 16, dot, 1);
+        QTile::read_col4(Qb, qrow0 + 32 * u, dt * 16, qtr, 0);
+        QTile::read_col4(Qb, qrow0 + 32 * u + 16, dt * 16, qtr, 1);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          dv[dt][kt] = E::mma(dot, pf[kt], dv[dt][kt]);
+          dk[dt][kt] = E::mma(qtr, sf[kt], dk[dt][kt]);
+        }
       }
     }
+  };
 
-    if (t + 1 < cnt) {
-      if (NBUF == 1) __syncthreads();  // every wave is done with the only stage
-      lstore(NBUF == 2 ? (buf ^ 1) : 0);
+  if constexpr (NS == 2) {
+    auto block = [&](int t, const char* stage, char* next) {
+      const int i = block_of(t);
+      const int in = t + 1 < cnt ? block_of(t + 1) : 0;
+      wait_vmem();
+      __syncthreads();
+      if (t + 1 < cnt) issue(next, in);
+      compute(i, stage);
+    };
+    for (int t = 0; t < cnt; t += 2) {
+      block(t, stage0, stage1);
+      if (t + 1 < cnt) block(t + 1, stage1, stage0);
     }
-    __syncthreads();
+  } else {
+    for (int t = 0; t < cnt; ++t) {
+      const int i = block_of(t);
+      const int in = t + 1 < cnt ? block_of(t + 1) : 0;
+      wait_vmem();
+      __syncthreads();
+      compute(i, stage0);
+      __syncthreads();  // every wave is done with the only stage
+      if (t + 1 < cnt) issue(stage0, in);
+    }
   }
 
-  if (key < N) {
-    T* dK = (T*)a.dk + head + (size_t)key * D;
-    T* dV = (T*)a.dv + head + (size_t)key * D;
+  // add the query halves: waves with qh = 1 hand their partial sums to qh = 0 via LDS,
+  // one tensor at a time (DT * KT * 1 KB per wave)
+  f32x4* xfer = reinterpret_cast<f32x4*>(stage0);
+  auto reduce = [&](f32x4 (&acc)[DT][KT]) {
+    __syncthreads();
+    if (qh == 1) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      T ko[4], vo[4];
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ko[e] = (T)(dk[dt][e] * a.scale);
-        vo[e] = (T)dv[dt][e];
-      }
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<bf16x4*>(dK + dt * 16 + 4 * g) = bf16x4{ko[0], ko[1], ko[2], ko[3]};
-        *reinterpret_cast<bf16x4*>(dV + dt * 16 + 4 * g) = bf16x4{vo[0], vo[1], vo[2], vo[3]};
-      } else {
-        *reinterpret_cast<f32x4*>(dK + dt * 16 + 4 * g) = f32x4{ko[0], ko[1], ko[2], ko[3]};
-        *reinterpret_cast<f32x4*>(dV + dt * 16 + 4 * g) = f32x4{vo[0], vo[1], vo[2], vo[3]};
+        for (int kt = 0; kt < KT; ++kt) xfer[((kh * DT + dt) * KT + kt) * 64 + l] = acc[dt][kt];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) acc[dt][kt] += xfer[((kh * DT + dt) * KT + kt) * 64 + l];
+    }
+  };
+  reduce(dk);
+  reduce(dv);
+
+  if (qh == 0) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const int key = k0 + kt * 16 + c16;
+      if (key >= N) continue;
+      T* dK = (T*)a.dk + head + (size_t)key * D;
+      T* dV = (T*)a.dv + head + (size_t)key * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        T ko[4], vo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ko[e] = (T)(dk[dt][kt][e] * a.scale);
+          vo[e] = (T)dv[dt][kt][e];
+        }
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dK + dt * 16 + 4 * g) = bf16x4{ko[0], ko[1], ko[2], ko[3]};
+          *reinterpret_cast<bf16x4*>(dV + dt * 16 + 4 * g) = bf16x4{vo[0], vo[1], vo[2], vo[3]};
+        } else {
+          *reinterpret_cast<f32x4*>(dK + dt * 16 + 4 * g) = f32x4{ko[0], ko[1], ko[2], ko[3]};
+          *reinterpret_cast<f32x4*>(dV + dt * 16 + 4 * g) = f32x4{vo[0], vo[1], vo[2], vo[3]};
+        }
       }
     }
   }
