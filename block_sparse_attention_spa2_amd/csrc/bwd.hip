@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 //   S^T = K Q^T, dP^T = V dO^T (A = K, V rows from LDS; B = Q, dO in registers),
 //   dS^T = P^T * (dP^T - Dv), dQ^T += K^T dS^T (A = K^T via transpose reads).
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int BQ>
+template <typename T, int D, int BQ, bool DENSE>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const T* dO = (const T*)a.dout + head;
   const int q0 = qb * BQ + w * 16 * QT;
 
-  const bool dense = a.row_cnt == nullptr;
+  constexpr bool dense = DENSE;
   const int cnt = dense ? a.Tn : a.row_cnt[item];
   ListCursor cur;
   if (!dense) cur.init(a.row_idx + (size_t)item * a.Tn, cnt);
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 //   dS = P * (dP - Dv), dV^T += dO^T P, dK^T += Q^T dS (A via transpose reads).
 // At the end the two query halves' partial sums are added through LDS.
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int BQ>
+template <typename T, int D, int BQ, bool DENSE>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int k0 = kb * BKV + kh * 32;  // first key of this wave
   const int qrow0 = qh * (BQ / 2);    // first query row of this wave within a query block
 
-  const bool dense = a.col_cnt == nullptr;
+  constexpr bool dense = DENSE;
   const int cnt = dense ? a.Tm : a.col_cnt[item];
   ListCursor cur;
   if (!dense) cur.init(a.col_idx + (size_t)item * a.Tm, cnt);
@@ -525,8 +525,14 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
 #define SPA2_BWD(T, D, BQ)                                                       \
   do {                                                                           \
     if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);        \
-    if (stages & kBwdDkdv) bwd_dkdv_kernel<T, D, BQ><<<gk, 256, 0, st>>>(a);     \
-    if (stages & kBwdDq) bwd_dq_kernel<T, D, BQ><<<gq, 256, 0, st>>>(a);         \
+    if (stages & kBwdDkdv) {                                                     \
+      if (m) bwd_dkdv_kernel<T, D, BQ, false><<<gk, 256, 0, st>>>(a);           \
+      else bwd_dkdv_kernel<T, D, BQ, true><<<gk, 256, 0, st>>>(a);              \
+    }                                                                            \
+    if (stages & kBwdDq) {                                                       \
+      if (m) bwd_dq_kernel<T, D, BQ, false><<<gq, 256, 0, st>>>(a);             \
+      else bwd_dq_kernel<T, D, BQ, true><<<gq, 256, 0, st>>>(a);                \
+    }                                                                            \
   } while (0)
   if (s.dtype == SPA2_BF16) {
     if (s.D == 64) {

@@ -156,6 +156,27 @@ __device__ __forceinline__ typename Elem<T>::frag load_row8(const T* p) {
   return *reinterpret_cast<const typename Elem<T>::frag*>(p);
 }
 
+// Streaming accesses (read or written once per kernel): non-temporal, so they do not push
+// the K/V tiles that many workgroups re-read out of the caches.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag load_row8_stream(const T* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(q));
+  } else {
+    const u32x4 lo = __builtin_nontemporal_load(q), hi = __builtin_nontemporal_load(q + 1);
+    return Elem<float>::pack(__builtin_bit_cast(f32x4, lo), __builtin_bit_cast(f32x4, hi));
+  }
+}
+__device__ __forceinline__ void store4_stream(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void store4_stream(bf16* p, f32x4 v) {
+  const bf16x4 b{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, b),
+                              reinterpret_cast<unsigned long long*>(p));
+}
+
 // ------------------------------------------------------------------------------------
 // Row-major LDS tile of ROWS x D elements, 16-byte chunks XOR-swizzled per row so that
 // both the 16-lane row reads (16 rows, one chunk) and the transpose reads (4 rows, two

@@ -40,7 +40,7 @@ struct FwdArgs {
 // Rescale threshold in log2 units: probabilities stay below 2^8 between rescales.
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int D, int BQ>
+template <typename T, int D, int BQ, bool DENSE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const T* V = (const T*)a.v + head;
   const int q0 = qb * BQ + w * 16 * QT;
 
-  const bool dense = a.row_cnt == nullptr;
+  constexpr bool dense = DENSE;  // dense: every key block, no list
   const int cnt = dense ? a.Tn : a.row_cnt[item];
   ListCursor cur;
   if (!dense) cur.init(a.row_idx + (size_t)item * a.Tn, cnt);
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int row = q0 + qt * 16 + c16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[qt][ks] = row < N ? load_row8<T>(Q + (size_t)row * D + ks * 32 + 8 * g) : E::zero();
+      qf[qt][ks] = row < N ? load_row8_stream<T>(Q + (size_t)row * D + ks * 32 + 8 * g) : E::zero();
   }
 
   f32x4 oacc[DT][QT];
@@ -206,21 +206,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if (row < N) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        T outv[4];
-        f32x4 of;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          of[e] = oacc[dt][qt][e] * inv;
-          outv[e] = (T)of[e];
-        }
-        if (a.o_f32)
-          *reinterpret_cast<f32x4*>(a.o_f32 + head + (size_t)row * D + dt * 16 + 4 * g) = of;
-        T* dst = O + (size_t)row * D + dt * 16 + 4 * g;
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<bf16x4*>(dst) = bf16x4{outv[0], outv[1], outv[2], outv[3]};
-        } else {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{outv[0], outv[1], outv[2], outv[3]};
-        }
+        const f32x4 of = oacc[dt][qt] * inv;
+        if (a.o_f32) store4_stream(a.o_f32 + head + (size_t)row * D + dt * 16 + 4 * g, of);
+        store4_stream(O + (size_t)row * D + dt * 16 + 4 * g, of);
       }
       if (g == 0) lse[row] = lt > 0.f ? (mrow[qt] + __log2f(lt)) * kLn2 : -INFINITY;
     }
@@ -233,7 +221,11 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
   FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, s.N, s.Tm, s.Tn, s.BH() * s.Tm,
             (float)(1.4426950408889634 / sqrt((double)s.D))};
   const dim3 grid(s.BH() * s.Tm);
-#define SPA2_FWD(T, D, BQ) fwd_kernel<T, D, BQ><<<grid, 256, 0, st>>>(a)
+#define SPA2_FWD(T, D, BQ)                                               \
+  do {                                                                   \
+    if (row_cnt) fwd_kernel<T, D, BQ, false><<<grid, 256, 0, st>>>(a);   \
+    else fwd_kernel<T, D, BQ, true><<<grid, 256, 0, st>>>(a);            \
+  } while (0)
   if (s.dtype == SPA2_BF16) {
     if (s.D == 64) {
       if (s.BQ == 64) SPA2_FWD(bf16, 64, 64); else SPA2_FWD(bf16, 64, 128);

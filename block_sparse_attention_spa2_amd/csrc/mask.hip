@@ -12,6 +12,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ 
 }
 
 // ------------------------------------------------------------------------------------
-// Workgroup reductions / scan over 256 threads (4 waves).
+// Wave-level reductions and scans (64 lanes; no workgroup barrier involved).
 // ------------------------------------------------------------------------------------
 __device__ __forceinline__ double wave_max(double x) {
 #pragma unroll
@@ -147,176 +149,236 @@ __device__ __forceinline__ int wave_isum(int x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-
-__device__ double block_max(double x, double* scratch) {
-  x = wave_max(x);
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
-  __syncthreads();
-  const double r = fmax(fmax(scratch[0], scratch[1]), fmax(scratch[2], scratch[3]));
-  __syncthreads();
-  return r;
-}
-__device__ double block_sum(double x, double* scratch) {
-  x = wave_sum(x);
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
-  __syncthreads();
-  const double r = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
-  __syncthreads();
-  return r;
-}
-__device__ int block_isum(int x, int* scratch) {
-  x = wave_isum(x);
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
-  __syncthreads();
-  const int r = scratch[0] + scratch[1] + scratch[2] + scratch[3];
-  __syncthreads();
-  return r;
-}
-// Exclusive prefix over threads in thread order (double).
-__device__ double block_excl_scan(double x, double* scratch) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+// exclusive prefix over lanes, in lane order
+__device__ __forceinline__ double wave_excl_scan(double x) {
+  const int l = lane_id();
   double inc = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const double y = __shfl_up(inc, o);
     if (l >= o) inc += y;
   }
-  if (l == 63) scratch[w] = inc;
   const double up = __shfl_up(inc, 1);
-  const double excl = l == 0 ? 0.0 : up;  // exclusive within the wave, no subtraction
-  __syncthreads();
-  double before = 0.0;
-  for (int i = 0; i < w; ++i) before += scratch[i];
-  __syncthreads();
-  return before + excl;
+  return l == 0 ? 0.0 : up;  // no subtraction: the sum of the lanes before this one
 }
-__device__ int block_excl_iscan(int x, int* scratch) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ int wave_excl_iscan(int x) {
+  const int l = lane_id();
   int inc = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(inc, o);
     if (l >= o) inc += y;
   }
-  if (l == 63) scratch[w] = inc;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += scratch[i];
-  __syncthreads();
-  return before + inc - x;
+  return inc - x;
+}
+// Orders this wave's LDS accesses: everything before is visible to every lane after.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
 // (value desc, index asc): true if (va, ia) comes before (vb, ib)
 __device__ __forceinline__ bool before(double va, int ia, double vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 // ------------------------------------------------------------------------------------
-// Per-row selection: one workgroup per (head, query block).
+// Per-row selection: one wave per (head, query block); the workgroup's waves work on
+// independent rows in their own LDS slices, so no workgroup barrier is needed.
 //   1. (from scores) P-bar row = exp(s - max) / sum, optionally stored;
-//   2. bitonic sort of (P-bar, index) pairs in LDS into (value desc, index asc) order;
-//   3. exclusive prefix sums in that order; n_p = #ranks whose prefix is below p;
-//   4. keep the first L = max(n_k, n_p) ranks (Top-k U Top-p is a prefix of the order);
-//   5. write the mask row and the ascending kept-index list.
-// Dynamic LDS: sort_n doubles + sort_n ints + sort_n bytes.
+//   2. candidates: the largest threshold tau (found by bisection) such that the blocks
+//      with P-bar >= tau number at least n_k and carry mass >= p (plus a rounding
+//      margin). Those blocks are the first ranks of the (value desc, index asc) order,
+//      and that prefix already reaches both the Top-k count and the Top-p mass, so
+//      Top-k U Top-p lies inside it. Only the candidates need sorting (all blocks when
+//      the row is flat enough);
+//   3. bitonic sort of the candidate (P-bar, index) pairs into (value desc, index asc);
+//   4. exclusive prefix sums in that order; n_p = #ranks whose prefix is below p;
+//   5. keep the first L = max(n_k, n_p) ranks (Top-k U Top-p is a prefix of the order);
+//   6. write the mask row and the ascending kept-index list.
+// Dynamic LDS per wave: 21 * sort_n bytes (row, candidates, indices, flags).
 // ------------------------------------------------------------------------------------
 template <bool FROM_SCORES>
 __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ src,
-                                                     double* __restrict__ pbar_out, int Tm, int Tn,
-                                                     int sort_n, int n_k, double p_frac,
+                                                     double* __restrict__ pbar_out, int rows,
+                                                     int Tn, int sort_n, int n_k, double p_frac,
                                                      uint8_t* __restrict__ mask,
                                                      int32_t* __restrict__ row_cnt,
                                                      int32_t* __restrict__ row_idx) {
   extern __shared__ __attribute__((aligned(16))) char sel_smem[];
-  double* val = reinterpret_cast<double*>(sel_smem);
+  const int l = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * (blockDim.x >> 6) + wave;  // (bh, i) flattened
+  if (row >= rows) return;  // whole wave leaves; nothing below synchronises the workgroup
+  char* mine = sel_smem + (size_t)wave * (((size_t)sort_n * 21 + 15) & ~(size_t)15);
+  double* pv = reinterpret_cast<double*>(mine);  // the row, by block index
+  double* val = pv + sort_n;                      // candidates, then sorted
   int* idx = reinterpret_cast<int*>(val + sort_n);
   uint8_t* keep = reinterpret_cast<uint8_t*>(idx + sort_n);
-  __shared__ double dscr[4];
-  __shared__ int iscr[4];
-
-  const int row = blockIdx.x;  // (bh, i) flattened
-  const int tid = threadIdx.x;
   const double* in = src + (size_t)row * Tn;
 
   // 1. the row's probabilities
+  double vmax = -DBL_MAX;
   if (FROM_SCORES) {
     double mx = -DBL_MAX;
-    for (int j = tid; j < Tn; j += 256) mx = fmax(mx, in[j]);
-    mx = block_max(mx, dscr);
+#pragma unroll 4
+    for (int j = l; j < Tn; j += 64) {
+      const double sv = in[j];
+      pv[j] = sv;
+      mx = fmax(mx, sv);
+    }
+    mx = wave_max(mx);
     double sm = 0.0;
-    for (int j = tid; j < Tn; j += 256) {
-      const double e = exp(in[j] - mx);
-      val[j] = e;
+    for (int j = l; j < Tn; j += 64) {
+      const double e = exp(pv[j] - mx);
+      pv[j] = e;
       sm += e;
     }
-    sm = block_sum(sm, dscr);
-    for (int j = tid; j < Tn; j += 256) {
-      const double pv = val[j] / sm;
-      val[j] = pv;
-      if (pbar_out) pbar_out[(size_t)row * Tn + j] = pv;
+    sm = wave_sum(sm);
+    for (int j = l; j < Tn; j += 64) {
+      const double p = pv[j] / sm;
+      pv[j] = p;
+      vmax = fmax(vmax, p);
+      if (pbar_out) pbar_out[(size_t)row * Tn + j] = p;
     }
   } else {
-    for (int j = tid; j < Tn; j += 256) val[j] = in[j];
+#pragma unroll 4
+    for (int j = l; j < Tn; j += 64) {
+      const double p = in[j];
+      pv[j] = p;
+      vmax = fmax(vmax, p);
+    }
   }
-  for (int j = tid; j < sort_n; j += 256) {
-    if (j >= Tn) val[j] = -1.0;  // padding sorts after every probability
-    idx[j] = j;
-  }
-  __syncthreads();
+  vmax = wave_max(vmax);
+  wave_lds_sync();
 
-  // 2. bitonic sort into (value desc, index asc)
-  const int half = sort_n >> 1;
-  for (int kk = 2; kk <= sort_n; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int pr = tid; pr < half; pr += 256) {
-        const int i1 = 2 * jj * (pr / jj) + (pr % jj);
-        const int i2 = i1 + jj;
-        const double v1 = val[i1], v2 = val[i2];
-        const int x1 = idx[i1], x2 = idx[i2];
-        const bool fwd = (i1 & kk) == 0;  // this half-block is ordered in the primary order
-        const bool swap = fwd ? before(v2, x2, v1, x1) : before(v1, x1, v2, x2);
-        if (swap) {
-          val[i1] = v2;
-          val[i2] = v1;
-          idx[i1] = x2;
-          idx[i2] = x1;
+  // 2. candidate threshold; lane l owns the contiguous block range [c_lo, c_hi)
+  const int per = (Tn + 63) / 64;
+  const int c_lo = min(Tn, l * per), c_hi = min(Tn, c_lo + per);
+  const double need = p_frac > 0.0 ? p_frac + 1e-12 : 0.0;  // margin over summation order
+  auto probe = [&](double tau, int& c, double& m) {
+    int cl = 0;
+    double ml = 0.0;
+    for (int j = c_lo; j < c_hi; ++j) {
+      const double v = pv[j];
+      if (v >= tau) {
+        ++cl;
+        ml += v;
+      }
+    }
+    c = wave_isum(cl);
+    m = wave_sum(ml);
+  };
+  double tau = -1.0;  // every block
+  {
+    int c;
+    double m;
+    probe(0.0, c, m);
+    if (c >= n_k && m >= need) {
+      double lo = 0.0, hi = vmax * 2.0 + 1e-300;  // lo valid, hi not (no block reaches it)
+      for (int it = 0; it < 40; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        probe(mid, c, m);
+        if (c >= n_k && m >= need) {
+          lo = mid;
+          if (c <= 64) break;  // few enough to sort
+        } else {
+          hi = mid;
         }
       }
-      __syncthreads();
+      tau = lo;
     }
   }
 
-  // 3. exclusive prefix mass over ranks 0 .. Tn-1; thread t owns a contiguous rank range
-  const int per = (Tn + 255) / 256;
-  const int r_lo = min(Tn, tid * per), r_hi = min(Tn, r_lo + per);
+  // gather the candidates in block order
+  int cl = 0;
+  for (int j = c_lo; j < c_hi; ++j) cl += pv[j] >= tau;
+  int pos = wave_excl_iscan(cl);
+  const int cand = wave_isum(cl);
+  for (int j = c_lo; j < c_hi; ++j)
+    if (pv[j] >= tau) {
+      val[pos] = pv[j];
+      idx[pos] = j;
+      ++pos;
+    }
+  int sn = 2;
+  while (sn < cand) sn <<= 1;
+  for (int j = cand + l; j < sn; j += 64) {
+    val[j] = -1.0;  // padding sorts after every probability
+    idx[j] = Tn + j;
+  }
+  wave_lds_sync();
+
+  // 3. bitonic sort into (value desc, index asc); each lane keeps up to four
+  // compare-exchange pairs in flight per pass, without branches
+  const int half = sn >> 1;
+  for (int kk = 2; kk <= sn; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      const int lg = __builtin_ctz(jj);
+      for (int base = 0; base < half; base += 256) {
+        int i1[4], i2[4];
+        double v1[4], v2[4];
+        int x1[4], x2[4];
+        bool act[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int pr = base + q * 64 + l;
+          act[q] = pr < half;
+          i1[q] = ((pr >> lg) << (lg + 1)) + (pr & (jj - 1));
+          i2[q] = i1[q] + jj;
+          if (act[q]) {
+            v1[q] = val[i1[q]];
+            v2[q] = val[i2[q]];
+            x1[q] = idx[i1[q]];
+            x2[q] = idx[i2[q]];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (!act[q]) continue;
+          const bool fwd = (i1[q] & kk) == 0;  // this half-block runs in the primary order
+          const bool b21 = before(v2[q], x2[q], v1[q], x1[q]);
+          const bool swap = fwd ? b21 : !b21;   // pairs never tie: indices differ
+          val[i1[q]] = swap ? v2[q] : v1[q];
+          val[i2[q]] = swap ? v1[q] : v2[q];
+          idx[i1[q]] = swap ? x2[q] : x1[q];
+          idx[i2[q]] = swap ? x1[q] : x2[q];
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+
+  // 4. exclusive prefix mass over the candidate ranks; lane l owns a contiguous range
+  const int rper = (cand + 63) / 64;
+  const int r_lo = min(cand, l * rper), r_hi = min(cand, r_lo + rper);
   double local = 0.0;
   for (int r = r_lo; r < r_hi; ++r) local += val[r];
-  double run = block_excl_scan(local, dscr);
+  double run = wave_excl_scan(local);
   int below = 0;
   for (int r = r_lo; r < r_hi; ++r) {
     if (run < p_frac) ++below;
     run += val[r];
   }
-  const int n_p = block_isum(below, iscr);
-  const int L = max(n_k, n_p);
+  const int n_p = wave_isum(below);
+  const int L = min(cand, max(n_k, n_p));  // cand >= both by the choice of tau
 
-  // 4. flag the first L ranks
-  for (int j = tid; j < Tn; j += 256) keep[j] = 0;
-  __syncthreads();
-  for (int r = tid; r < L; r += 256) keep[idx[r]] = 1;
-  __syncthreads();
+  // 5. flag the first L ranks
+  for (int j = l; j < Tn; j += 64) keep[j] = 0;
+  wave_lds_sync();
+  for (int r = l; r < L; r += 64) keep[idx[r]] = 1;
+  wave_lds_sync();
 
-  // 5. mask row and ascending compaction
+  // 6. mask row and ascending compaction
   uint8_t* mrow = mask + (size_t)row * Tn;
-  for (int j = tid; j < Tn; j += 256) mrow[j] = keep[j];
-  const int c_lo = min(Tn, tid * per), c_hi = min(Tn, c_lo + per);
+  for (int j = l; j < Tn; j += 64) mrow[j] = keep[j];
   int cnt = 0;
   for (int j = c_lo; j < c_hi; ++j) cnt += keep[j];
-  int pos = block_excl_iscan(cnt, iscr);
+  int opos = wave_excl_iscan(cnt);
   int32_t* out = row_idx + (size_t)row * Tn;
   for (int j = c_lo; j < c_hi; ++j)
-    if (keep[j]) out[pos++] = j;
-  if (tid == 0) row_cnt[row] = L;
+    if (keep[j]) out[opos++] = j;
+  if (l == 0) row_cnt[row] = L;
 }
 
 // Row lists from a caller-filled mask (one thread per row).
@@ -332,18 +394,33 @@ __global__ void rows_kernel(const uint8_t* __restrict__ mask, int rows, int Tn,
   row_cnt[r] = c;
 }
 
-// Column lists: thread per key block; reads mask rows coalesced across threads.
-__global__ void cols_kernel(const uint8_t* __restrict__ mask, int Tm, int Tn, int col_groups,
-                            int32_t* __restrict__ col_cnt, int32_t* __restrict__ col_idx) {
+// Column lists: a workgroup covers 16 key blocks (columns) of one head; its 256 threads
+// are 16 columns x 16 slices of the query-block rows. Each thread counts its slice, the
+// counts are scanned over slices in LDS, and a second pass writes the ascending indices.
+__global__ __launch_bounds__(256) void cols_kernel(const uint8_t* __restrict__ mask, int Tm,
+                                                   int Tn, int col_groups,
+                                                   int32_t* __restrict__ col_cnt,
+                                                   int32_t* __restrict__ col_idx) {
+  __shared__ int cnts[16][17];
   const int bh = blockIdx.x / col_groups;
-  const int j = (blockIdx.x % col_groups) * blockDim.x + threadIdx.x;
-  if (j >= Tn) return;
+  const int c = threadIdx.x & 15, part = threadIdx.x >> 4;
+  const int j = (blockIdx.x % col_groups) * 16 + c;
+  const int rp = (Tm + 15) / 16;
+  const int i0 = min(Tm, part * rp), i1 = min(Tm, i0 + rp);
   const uint8_t* m = mask + (size_t)bh * Tm * Tn;
-  int32_t* out = col_idx + ((size_t)bh * Tn + j) * Tm;
-  int c = 0;
-  for (int i = 0; i < Tm; ++i)
-    if (m[(size_t)i * Tn + j]) out[c++] = i;
-  col_cnt[(size_t)bh * Tn + j] = c;
+  int n = 0;
+  if (j < Tn)
+    for (int i = i0; i < i1; ++i) n += m[(size_t)i * Tn + j];
+  cnts[part][c] = n;
+  __syncthreads();
+  int off = 0;
+  for (int p = 0; p < part; ++p) off += cnts[p][c];
+  if (j < Tn) {
+    int32_t* out = col_idx + ((size_t)bh * Tn + j) * Tm;
+    for (int i = i0; i < i1; ++i)
+      if (m[(size_t)i * Tn + j]) out[off++] = i;
+    if (part == 15) col_cnt[(size_t)bh * Tn + j] = off;
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -385,14 +462,23 @@ static int sort_size(int tn) {
 hipError_t launch_select(const Shape& s, const double* src, bool from_scores, double* pbar_out,
                          int n_k, double p_frac, const spa2_blockmask& m, hipStream_t st) {
   const int sn = sort_size(s.Tn);
-  const size_t lds = (size_t)sn * (sizeof(double) + sizeof(int) + 1);
-  const dim3 grid(s.BH() * s.Tm);
-  if (from_scores)
-    select_kernel<true><<<grid, 256, lds, st>>>(src, pbar_out, s.Tm, s.Tn, sn, n_k, p_frac,
-                                                m.mask, m.row_cnt, m.row_idx);
-  else
-    select_kernel<false><<<grid, 256, lds, st>>>(src, nullptr, s.Tm, s.Tn, sn, n_k, p_frac,
-                                                 m.mask, m.row_cnt, m.row_idx);
+  const size_t per_wave = ((size_t)sn * 21 + 15) & ~(size_t)15;  // 2 doubles + int + byte
+  // rows per workgroup: up to 4 waves, as many as fit in 160 KB of LDS
+  const int wpg = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / per_wave));
+  const int rows = s.BH() * s.Tm;
+  const dim3 grid((rows + wpg - 1) / wpg);
+  const size_t lds = per_wave * wpg;
+  if (from_scores) {
+    hipFuncSetAttribute((const void*)select_kernel<true>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    select_kernel<true><<<grid, 64 * wpg, lds, st>>>(src, pbar_out, rows, s.Tn, sn, n_k, p_frac,
+                                                     m.mask, m.row_cnt, m.row_idx);
+  } else {
+    hipFuncSetAttribute((const void*)select_kernel<false>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    select_kernel<false><<<grid, 64 * wpg, lds, st>>>(src, nullptr, rows, s.Tn, sn, n_k, p_frac,
+                                                      m.mask, m.row_cnt, m.row_idx);
+  }
   return hipGetLastError();
 }
 
@@ -403,7 +489,7 @@ hipError_t launch_rows(const Shape& s, const spa2_blockmask& m, hipStream_t st) 
 }
 
 hipError_t launch_cols(const Shape& s, const spa2_blockmask& m, hipStream_t st) {
-  const int groups = (s.Tn + 255) / 256;
+  const int groups = (s.Tn + 15) / 16;
   cols_kernel<<<s.BH() * groups, 256, 0, st>>>(m.mask, s.Tm, s.Tn, groups, m.col_cnt, m.col_idx);
   return hipGetLastError();
 }
