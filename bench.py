@@ -29,8 +29,66 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 
+KERNEL_SOURCES = {
+    "fwd": ("fwd.hip", "common.h", "kernels.h"),
+    "bwd_dkdv": ("bwd.hip", "common.h", "kernels.h"),
+    "bwd_dq": ("bwd.hip", "common.h", "kernels.h"),
+}
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_wan13b_480p.txt")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_digest(kernel):
+    """SHA-256 of a kernel's HIP sources with comments and blank space removed, plus the
+    compiler flags: a recorded counter reading applies only while this is unchanged."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "block_sparse_attention_spa2_amd", "csrc")
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(name.encode())
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
+    from block_sparse_attention_spa2_amd import build
+    h.update(" ".join(build.FLAGS).encode())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or None when there is
+    no record for this kernel and workload or the kernel changed since it was taken."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if not line.startswith("RECORD "):
+                continue
+            rec = json.loads(line[len("RECORD "):])
+            if rec["kernel"] == kernel and rec["workload"] == workload:
+                if rec["source_sha256"] != kernel_digest(kernel):
+                    return None
+                return rec["bytes_per_launch"]
+    return None
+
+
+def copy_calibration():
+    """A plain device-to-device copy of a known size (512 MiB, three times), run under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to scale those counters to bytes."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n * 2, "launches": 3}), flush=True)
 
 
 def kept_area(mask, n, bq, bkv):
@@ -51,11 +109,16 @@ def main():
     ap.add_argument("--no-check", action="store_true", help="skip the oracle parity check")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--dense-reps", type=int, default=2)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus "
               f"{args.gpus}", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -166,7 +229,8 @@ def main():
     achieved = kernel_flops[dom] / (per_stage[dom] * 1e-3) / 1e12
     roofline = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2),
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                    traffic=recorded_traffic(dom, args.workload),
                     flops_per_launch=kernel_flops[dom], ms_per_launch=round(per_stage[dom], 4))
     mask_bytes = 2.0 * B * H * N * D * q.element_size()  # Q and K read once
 

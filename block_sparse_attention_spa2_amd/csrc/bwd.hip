@@ -10,7 +10,9 @@
 // Three deterministic kernels:
 //   bwd_pre   Dv = rowsum(dO * O) (fp32), one pass over O and dO;
 //   bwd_dkdv  one workgroup per key block, looping over the query blocks that keep it
-//             (column lists); wave w owns 16 keys; Q_i and dO_i are staged in LDS;
+//             (column lists); the four waves split the block 2 x 2 (key halves of 32
+//             x query halves), Q_i and dO_i are staged in LDS, and the two query
+//             halves' partial dK/dV are summed through LDS at the end;
 //   bwd_dq    one workgroup per query block, looping over its kept key blocks (row
 //             lists), like the forward; K_j and V_j are staged in LDS.
 #include <math.h>
