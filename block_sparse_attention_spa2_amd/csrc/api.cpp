@@ -28,7 +28,7 @@ spa2_status check_desc(const spa2_desc* d, spa2::Shape* out) {
   if (d->BQ != 64 && d->BQ != 128) return SPA2_E_SHAPE;
   if (d->BKV != 64) return SPA2_E_SHAPE;
   const int tn = blocks(d->N, d->BKV);
-  if (tn > spa2::kMaxSort) return SPA2_E_SHAPE;
+  if (tn > spa2::kMaxTn) return SPA2_E_SHAPE;
   *out = spa2::Shape{d->B, d->H, d->N, d->D, d->BQ, d->BKV, d->dtype, blocks(d->N, d->BQ), tn};
   return SPA2_OK;
 }

@@ -14,8 +14,9 @@ struct Shape {
   int BH() const { return B * H; }
 };
 
-// Largest key-block count the selection kernel sorts (power of two).
-constexpr int kMaxSort = 4096;
+// Largest key-block count per row: the selection kernel holds a row in registers, 64 blocks
+// per lane at most.
+constexpr int kMaxTn = 4096;
 
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar,
                        hipStream_t st);

@@ -144,241 +144,182 @@ __device__ __forceinline__ double wave_sum(double x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-__device__ __forceinline__ int wave_isum(int x) {
+// Cross-lane moves on the VALU (no LDS round trip) for the selection's inner loop.
+// DPP quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror; then the 16- and
+// 32-lane swaps. Each step pairs lanes symmetrically, so every lane ends with the same
+// result.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+template <bool W32>
+__device__ __forceinline__ double swap_max_f64(double x) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = (unsigned)u, hi = (unsigned)(u >> 32);
+  const auto rl = W32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                      : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto rh = W32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                      : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const double a = __builtin_bit_cast(double, ((unsigned long long)(unsigned)rh[0] << 32) | (unsigned)rl[0]);
+  const double b = __builtin_bit_cast(double, ((unsigned long long)(unsigned)rh[1] << 32) | (unsigned)rl[1]);
+  return fmax(a, b);
+}
+__device__ __forceinline__ double wave_max_fast(double x) {
+  x = fmax(x, dpp_f64<0xB1>(x));   // lane ^ 1
+  x = fmax(x, dpp_f64<0x4E>(x));   // lane ^ 2
+  x = fmax(x, dpp_f64<0x141>(x));  // mirror within 8
+  x = fmax(x, dpp_f64<0x140>(x));  // mirror within 16
+  x = swap_max_f64<false>(x);      // lanes l, l ^ 16
+  return swap_max_f64<true>(x);    // lanes l, l ^ 32
+}
+__device__ __forceinline__ int wave_min_int(int x) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
   return x;
 }
-// exclusive prefix over lanes, in lane order
-__device__ __forceinline__ double wave_excl_scan(double x) {
-  const int l = lane_id();
-  double inc = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(inc, o);
-    if (l >= o) inc += y;
-  }
-  const double up = __shfl_up(inc, 1);
-  return l == 0 ? 0.0 : up;  // no subtraction: the sum of the lanes before this one
-}
-__device__ __forceinline__ int wave_excl_iscan(int x) {
-  const int l = lane_id();
-  int inc = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (l >= o) inc += y;
-  }
-  return inc - x;
-}
-// Orders this wave's LDS accesses: everything before is visible to every lane after.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// (value desc, index asc): true if (va, ia) comes before (vb, ib)
-__device__ __forceinline__ bool before(double va, int ia, double vb, int ib) {
-  return (va > vb) | ((va == vb) & (ia < ib));
-}
 
 // ------------------------------------------------------------------------------------
-// Per-row selection: one wave per (head, query block); the workgroup's waves work on
-// independent rows in their own LDS slices, so no workgroup barrier is needed.
+// Per-row selection: one wave per (head, query block), the row held in registers
+// (lane l owns blocks j = l + 64 t, t < PER), no LDS.
 //   1. (from scores) P-bar row = exp(s - max) / sum, optionally stored;
-//   2. candidates: the largest threshold tau (found by bisection) such that the blocks
-//      with P-bar >= tau number at least n_k and carry mass >= p (plus a rounding
-//      margin). Those blocks are the first ranks of the (value desc, index asc) order,
-//      and that prefix already reaches both the Top-k count and the Top-p mass, so
-//      Top-k U Top-p lies inside it. Only the candidates need sorting (all blocks when
-//      the row is flat enough);
-//   3. bitonic sort of the candidate (P-bar, index) pairs into (value desc, index asc);
-//   4. exclusive prefix sums in that order; n_p = #ranks whose prefix is below p;
-//   5. keep the first L = max(n_k, n_p) ranks (Top-k U Top-p is a prefix of the order);
-//   6. write the mask row and the ascending kept-index list.
-// Dynamic LDS per wave: 21 * sort_n bytes (row, candidates, indices, flags).
+//   2. each lane keeps a small window: its W largest blocks in (value desc, index asc)
+//      order, refilled from its remaining blocks when used up;
+//   3. the row's order is produced one rank at a time: the largest window head over the
+//      wave (ties: the smallest block index) is rank r. Rank r is kept iff r < n_k or
+//      its exclusive prefix mass e_r (the running sum of the values already taken, in
+//      rank order) is below p. Both tests fail for good once they fail, so the first
+//      rejected rank ends the row: Top-k U Top-p is the prefix taken so far;
+//   4. mask row and the ascending kept-index list from the lanes' kept bits.
 // ------------------------------------------------------------------------------------
-template <bool FROM_SCORES>
+template <int PER, bool FROM_SCORES>
 __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ src,
                                                      double* __restrict__ pbar_out, int rows,
-                                                     int Tn, int sort_n, int n_k, double p_frac,
+                                                     int Tn, int n_k, double p_frac,
                                                      uint8_t* __restrict__ mask,
                                                      int32_t* __restrict__ row_cnt,
                                                      int32_t* __restrict__ row_idx) {
-  extern __shared__ __attribute__((aligned(16))) char sel_smem[];
+  constexpr int W = 4;  // window length
   const int l = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int row = blockIdx.x * (blockDim.x >> 6) + wave;  // (bh, i) flattened
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);  // (bh, i) flattened
   if (row >= rows) return;  // whole wave leaves; nothing below synchronises the workgroup
-  char* mine = sel_smem + (size_t)wave * (((size_t)sort_n * 21 + 15) & ~(size_t)15);
-  double* pv = reinterpret_cast<double*>(mine);  // the row, by block index
-  double* val = pv + sort_n;                      // candidates, then sorted
-  int* idx = reinterpret_cast<int*>(val + sort_n);
-  uint8_t* keep = reinterpret_cast<uint8_t*>(idx + sort_n);
+  const int tcnt = (Tn + 63) / 64;  // rounds that hold any block (wave-uniform)
   const double* in = src + (size_t)row * Tn;
 
-  // 1. the row's probabilities
-  double vmax = -DBL_MAX;
+  // 1. the row's probabilities; slots past the row hold -1
+  double v[PER];
   if (FROM_SCORES) {
     double mx = -DBL_MAX;
-#pragma unroll 4
-    for (int j = l; j < Tn; j += 64) {
-      const double sv = in[j];
-      pv[j] = sv;
-      mx = fmax(mx, sv);
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      v[t] = -DBL_MAX;
+      if (t < tcnt && l + 64 * t < Tn) v[t] = in[l + 64 * t];
+      mx = fmax(mx, v[t]);
     }
     mx = wave_max(mx);
     double sm = 0.0;
-    for (int j = l; j < Tn; j += 64) {
-      const double e = exp(pv[j] - mx);
-      pv[j] = e;
-      sm += e;
-    }
+#pragma unroll
+    for (int t = 0; t < PER; ++t)
+      if (t < tcnt && l + 64 * t < Tn) {
+        v[t] = exp(v[t] - mx);
+        sm += v[t];
+      }
     sm = wave_sum(sm);
-    for (int j = l; j < Tn; j += 64) {
-      const double p = pv[j] / sm;
-      pv[j] = p;
-      vmax = fmax(vmax, p);
-      if (pbar_out) pbar_out[(size_t)row * Tn + j] = p;
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      if (t < tcnt && l + 64 * t < Tn) {
+        v[t] = v[t] / sm;
+        if (pbar_out) pbar_out[(size_t)row * Tn + l + 64 * t] = v[t];
+      } else {
+        v[t] = -1.0;
+      }
     }
   } else {
-#pragma unroll 4
-    for (int j = l; j < Tn; j += 64) {
-      const double p = in[j];
-      pv[j] = p;
-      vmax = fmax(vmax, p);
-    }
-  }
-  vmax = wave_max(vmax);
-  wave_lds_sync();
-
-  // 2. candidate threshold; lane l owns the contiguous block range [c_lo, c_hi)
-  const int per = (Tn + 63) / 64;
-  const int c_lo = min(Tn, l * per), c_hi = min(Tn, c_lo + per);
-  const double need = p_frac > 0.0 ? p_frac + 1e-12 : 0.0;  // margin over summation order
-  auto probe = [&](double tau, int& c, double& m) {
-    int cl = 0;
-    double ml = 0.0;
-    for (int j = c_lo; j < c_hi; ++j) {
-      const double v = pv[j];
-      if (v >= tau) {
-        ++cl;
-        ml += v;
-      }
-    }
-    c = wave_isum(cl);
-    m = wave_sum(ml);
-  };
-  double tau = -1.0;  // every block
-  {
-    int c;
-    double m;
-    probe(0.0, c, m);
-    if (c >= n_k && m >= need) {
-      double lo = 0.0, hi = vmax * 2.0 + 1e-300;  // lo valid, hi not (no block reaches it)
-      for (int it = 0; it < 40; ++it) {
-        const double mid = 0.5 * (lo + hi);
-        probe(mid, c, m);
-        if (c >= n_k && m >= need) {
-          lo = mid;
-          if (c <= 64) break;  // few enough to sort
-        } else {
-          hi = mid;
-        }
-      }
-      tau = lo;
-    }
-  }
-
-  // gather the candidates in block order
-  int cl = 0;
-  for (int j = c_lo; j < c_hi; ++j) cl += pv[j] >= tau;
-  int pos = wave_excl_iscan(cl);
-  const int cand = wave_isum(cl);
-  for (int j = c_lo; j < c_hi; ++j)
-    if (pv[j] >= tau) {
-      val[pos] = pv[j];
-      idx[pos] = j;
-      ++pos;
-    }
-  int sn = 2;
-  while (sn < cand) sn <<= 1;
-  for (int j = cand + l; j < sn; j += 64) {
-    val[j] = -1.0;  // padding sorts after every probability
-    idx[j] = Tn + j;
-  }
-  wave_lds_sync();
-
-  // 3. bitonic sort into (value desc, index asc); each lane keeps up to four
-  // compare-exchange pairs in flight per pass, without branches
-  const int half = sn >> 1;
-  for (int kk = 2; kk <= sn; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      const int lg = __builtin_ctz(jj);
-      for (int base = 0; base < half; base += 256) {
-        int i1[4], i2[4];
-        double v1[4], v2[4];
-        int x1[4], x2[4];
-        bool act[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int pr = base + q * 64 + l;
-          act[q] = pr < half;
-          i1[q] = ((pr >> lg) << (lg + 1)) + (pr & (jj - 1));
-          i2[q] = i1[q] + jj;
-          if (act[q]) {
-            v1[q] = val[i1[q]];
-            v2[q] = val[i2[q]];
-            x1[q] = idx[i1[q]];
-            x2[q] = idx[i2[q]];
+    for (int t = 0; t < PER; ++t) v[t] = (t < tcnt && l + 64 * t < Tn) ? in[l + 64 * t] : -1.0;
+  }
+
+  // 2. window: the lane's W first blocks in order among those after (lv, lt)
+  double wv[W];
+  int wt[W];
+  auto refill = [&](double lv, int lt) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      wv[k] = -1.0;
+      wt[k] = 0;
+    }
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      if (t >= tcnt) break;
+      const double x = v[t];
+      const bool after = (x < lv) | ((x == lv) & (t > lt));
+      if (after && x > wv[W - 1]) {  // strictly larger: equal values keep index order
+        wv[W - 1] = x;
+        wt[W - 1] = t;
+#pragma unroll
+        for (int k = W - 1; k > 0; --k) {
+          if (wv[k] > wv[k - 1]) {
+            const double tv = wv[k];
+            wv[k] = wv[k - 1];
+            wv[k - 1] = tv;
+            const int tt = wt[k];
+            wt[k] = wt[k - 1];
+            wt[k - 1] = tt;
           }
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (!act[q]) continue;
-          const bool fwd = (i1[q] & kk) == 0;  // this half-block runs in the primary order
-          const bool b21 = before(v2[q], x2[q], v1[q], x1[q]);
-          const bool swap = fwd ? b21 : !b21;   // pairs never tie: indices differ
-          val[i1[q]] = swap ? v2[q] : v1[q];
-          val[i2[q]] = swap ? v1[q] : v2[q];
-          idx[i1[q]] = swap ? x2[q] : x1[q];
-          idx[i2[q]] = swap ? x1[q] : x2[q];
-        }
       }
-      wave_lds_sync();
     }
+  };
+  refill(2.0, -1);  // every block (all values are below 2)
+
+  // 3. ranks in order until the first rejected one
+  unsigned long long kept = 0;  // bit t: block l + 64 t is kept
+  double prefix = 0.0;          // e_r, summed in rank order
+  int rank = 0;
+  for (;;) {
+    const double m = wave_max_fast(wv[0]);
+    if (m < 0.0) break;                              // every block is kept
+    if (rank >= n_k && !(prefix < p_frac)) break;    // rank r fails both tests
+    const unsigned long long tie = __builtin_amdgcn_ballot_w64(wv[0] == m);
+    int owner = __builtin_ctzll(tie);
+    if ((tie & (tie - 1)) != 0)  // equal values in several lanes: smallest block index
+      owner = wave_min_int(wv[0] == m ? l + 64 * wt[0] : INT_MAX) & 63;
+    if (l == owner) {
+      const int lt = wt[0];
+      kept |= 1ull << lt;
+#pragma unroll
+      for (int k = 0; k < W - 1; ++k) {
+        wv[k] = wv[k + 1];
+        wt[k] = wt[k + 1];
+      }
+      wv[W - 1] = -1.0;
+      if (wv[0] < 0.0) refill(m, lt);
+    }
+    prefix += m;
+    ++rank;
   }
 
-  // 4. exclusive prefix mass over the candidate ranks; lane l owns a contiguous range
-  const int rper = (cand + 63) / 64;
-  const int r_lo = min(cand, l * rper), r_hi = min(cand, r_lo + rper);
-  double local = 0.0;
-  for (int r = r_lo; r < r_hi; ++r) local += val[r];
-  double run = wave_excl_scan(local);
-  int below = 0;
-  for (int r = r_lo; r < r_hi; ++r) {
-    if (run < p_frac) ++below;
-    run += val[r];
-  }
-  const int n_p = wave_isum(below);
-  const int L = min(cand, max(n_k, n_p));  // cand >= both by the choice of tau
-
-  // 5. flag the first L ranks
-  for (int j = l; j < Tn; j += 64) keep[j] = 0;
-  wave_lds_sync();
-  for (int r = l; r < L; r += 64) keep[idx[r]] = 1;
-  wave_lds_sync();
-
-  // 6. mask row and ascending compaction
+  // 4. mask row and ascending compaction (round t holds blocks 64 t .. 64 t + 63)
   uint8_t* mrow = mask + (size_t)row * Tn;
-  for (int j = l; j < Tn; j += 64) mrow[j] = keep[j];
-  int cnt = 0;
-  for (int j = c_lo; j < c_hi; ++j) cnt += keep[j];
-  int opos = wave_excl_iscan(cnt);
   int32_t* out = row_idx + (size_t)row * Tn;
-  for (int j = c_lo; j < c_hi; ++j)
-    if (keep[j]) out[opos++] = j;
-  if (l == 0) row_cnt[row] = L;
+  int base = 0;
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    if (t >= tcnt) break;
+    const int j = l + 64 * t;
+    const bool kb = (kept >> t) & 1;
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(kb);
+    if (j < Tn) mrow[j] = kb;
+    if (kb) {
+      const int pos = __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0));
+      out[base + pos] = j;
+    }
+    base += __builtin_popcountll(bal);
+  }
+  if (l == 0) row_cnt[row] = rank;
 }
 
 // Row lists from a caller-filled mask (one thread per row).
@@ -453,32 +394,25 @@ hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar,
   return hipGetLastError();
 }
 
-static int sort_size(int tn) {
-  int n = 2;
-  while (n < tn) n <<= 1;
-  return n;
-}
-
 hipError_t launch_select(const Shape& s, const double* src, bool from_scores, double* pbar_out,
                          int n_k, double p_frac, const spa2_blockmask& m, hipStream_t st) {
-  const int sn = sort_size(s.Tn);
-  const size_t per_wave = ((size_t)sn * 21 + 15) & ~(size_t)15;  // 2 doubles + int + byte
-  // rows per workgroup: up to 4 waves, as many as fit in 160 KB of LDS
-  const int wpg = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / per_wave));
   const int rows = s.BH() * s.Tm;
-  const dim3 grid((rows + wpg - 1) / wpg);
-  const size_t lds = per_wave * wpg;
-  if (from_scores) {
-    hipFuncSetAttribute((const void*)select_kernel<true>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    select_kernel<true><<<grid, 64 * wpg, lds, st>>>(src, pbar_out, rows, s.Tn, sn, n_k, p_frac,
-                                                     m.mask, m.row_cnt, m.row_idx);
-  } else {
-    hipFuncSetAttribute((const void*)select_kernel<false>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    select_kernel<false><<<grid, 64 * wpg, lds, st>>>(src, nullptr, rows, s.Tn, sn, n_k, p_frac,
-                                                      m.mask, m.row_cnt, m.row_idx);
-  }
+  const dim3 grid((rows + 3) / 4);  // four rows (waves) per workgroup
+  const int per = (s.Tn + 63) / 64;
+#define SPA2_SELECT(P)                                                                   \
+  do {                                                                                   \
+    if (from_scores)                                                                     \
+      select_kernel<P, true><<<grid, 256, 0, st>>>(src, pbar_out, rows, s.Tn, n_k,       \
+                                                   p_frac, m.mask, m.row_cnt, m.row_idx); \
+    else                                                                                 \
+      select_kernel<P, false><<<grid, 256, 0, st>>>(src, nullptr, rows, s.Tn, n_k,       \
+                                                    p_frac, m.mask, m.row_cnt, m.row_idx); \
+  } while (0)
+  if (per <= 8) SPA2_SELECT(8);
+  else if (per <= 16) SPA2_SELECT(16);
+  else if (per <= 32) SPA2_SELECT(32);
+  else SPA2_SELECT(64);
+#undef SPA2_SELECT
   return hipGetLastError();
 }
 

@@ -79,3 +79,48 @@ def test_staged_backward_equals_bwd(wan13b):
     dq = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], dvec, bm, torch.empty_like(o))
     for a, b in zip(g1, (dq, dk, dv)):
         assert torch.equal(a, b)
+
+
+@pytest.fixture(scope="module")
+def wan14b():
+    w = configs.params("wan14b_720p")
+    print(f"[wan14b_720p] drawing inputs, p={w['p']}", flush=True)
+    inp = configs.make_inputs("wan14b_720p")
+    mask, infos = gu.oracle_masks(inp, w["BQ"], w["BKV"], w["k"], w["p"])
+    dev = {x: gu.to_dev(getattr(inp, x)) for x in ("q", "k", "v")}
+    return dict(w=w, inp=inp, mask=mask, infos=infos, dev=dev)
+
+
+def test_wan14b_mask_all_heads(wan14b):
+    w, d = wan14b["w"], wan14b["dev"]
+    bm = spa2.mask(d["q"], d["k"], w["k"], w["p"], w["BQ"], w["BKV"])
+    g = bm.mask.cpu().numpy().astype(bool)
+    cls = gu.classify_mask(g, wan14b["mask"], wan14b["infos"])
+    print(f"[wan14b_720p] kept {g.mean():.6f} (oracle {wan14b['mask'].mean():.6f}); {cls}")
+    assert cls["other"] == 0 and cls["k_band"] == 0, cls
+    assert abs(wan14b["mask"].mean() - 0.05) < 1e-4
+    # the lists agree with the mask
+    cnt = bm.row_cnt.cpu().numpy()
+    assert np.array_equal(cnt, g.sum(-1))
+    ccnt = bm.col_cnt.cpu().numpy()
+    assert np.array_equal(ccnt, g.sum(-2))
+
+
+def test_wan14b_fwd_sampled(wan14b):
+    """Forward at the 720p shape (591 x 1182 block grid, q tail 80 rows, k tail 16 keys)
+    on three query blocks of every head, including the partial last one."""
+    w, d, inp = wan14b["w"], wan14b["dev"], wan14b["inp"]
+    bq, bkv, N = w["BQ"], w["BKV"], w["N"]
+    bm = spa2.mask(d["q"], d["k"], w["k"], w["p"], bq, bkv)
+    gm = bm.mask.cpu().numpy().astype(bool)
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm)
+    on, ln = gu.to_f64(o), lse.cpu().numpy().astype(np.float64)
+    tm = gm.shape[-2]
+    rng = np.random.default_rng(1)
+    for h in range(w["H"]):
+        q, k, v = (inp.head_f64(x, 0, h) for x in ("q", "k", "v"))
+        qblocks = sorted({0, tm - 1, int(rng.integers(tm))})
+        o_ref, lse_ref = oracle.attn_fwd_head(q, k, v, gm[0, h], bq, bkv, rows=qblocks)
+        qr = np.concatenate([np.arange(i * bq, min(N, (i + 1) * bq)) for i in qblocks])
+        gu.check_close(f"O h{h}", on[0, h][qr], o_ref[qr], "bf16")
+        gu.check_lse(ln[0, h][qr], lse_ref[qr], "bf16")
