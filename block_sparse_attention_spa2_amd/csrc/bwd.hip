@@ -78,6 +78,21 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // dQ: per query block, over its kept key blocks.
 //   S^T = K Q^T, dP^T = V dO^T (A = K, V rows from LDS; B = Q, dO in registers),
 //   dS^T = P^T * (dP^T - Dv), dQ^T += K^T dS^T (A = K^T via transpose reads).
+//
+// bf16 only: two rounding errors grow with a large offset c_j shared by a block's keys (an
+// attention-sink block), because each is multiplied by the keys:
+//  * rounding dS to bf16 leaves sum_k r_k K_k, r = dS - bf16(dS), whose offset part
+//    (sum_k r_k) c_j is added back;
+//  * the row term Dv carries the rounding of O, which shifts every dS_k by -P_k dDv. In
+//    exact arithmetic sum_k dS_k = 0 over the row, so the measured T = sum_k dS_k equals
+//    -dDv, and the shift's offset part T sum_j P^blk_j c_j (P^blk_j = the row's mass on
+//    block j) is removed at the end.
+// c_j = the block's first key row; what remains involves only K_k - c_j. Both terms are
+// rank-one updates per block, w_j (x) c_j with w_j = sum_k r_k or P^blk_j. They are
+// batched on the matrix unit: the c_j of 32 consecutive blocks are copied into an LDS
+// matrix C (32 x D) and the weights into an MFMA operand W (32 x 16 queries per tile), and
+// every 32 blocks acc += C^T W, pkc += C^T W'. sum_k bf16(dS_k) comes from the matrix unit
+// too (a ones operand times the packed dS), so sum_k r_k costs one add per element.
 // ------------------------------------------------------------------------------------
 template <typename T, int D, int BQ, bool DENSE>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
@@ -88,9 +103,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   using KV = Tile<T, BKV, D>;
+  constexpr bool kCorr = sizeof(T) == 2;
+  using CM = Tile<T, 32, D>;  // c_j of one batch of 32 blocks (bf16 only)
   // two stages in two LDS variables, named statically (see the forward kernel)
   __shared__ __attribute__((aligned(1024))) char stage0[2 * KV::kBytes];
   __shared__ __attribute__((aligned(1024))) char stage1[2 * KV::kBytes];
+  __shared__ __attribute__((aligned(1024))) char cm0[kCorr ? CM::kBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char cm1[kCorr ? CM::kBytes : 16];
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,6 +135,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     plan.issue_any(stage + KV::kBytes, V, j * BKV, N, w);
   };
   if (cnt > 0) issue(stage0, block_of(0));
+  if constexpr (kCorr) {  // C starts at zero: unfilled rows meet zero weights
+    const u32x4 z{0u, 0u, 0u, 0u};
+    for (int o = tid * 16; o < CM::kBytes; o += 256 * 16) {
+      *reinterpret_cast<u32x4*>(cm0 + o) = z;
+      *reinterpret_cast<u32x4*>(cm1 + o) = z;
+    }
+  }
 
   F qf[QT][KS], df[QT][KS];
   float lse2[QT], dv[QT];
@@ -132,20 +158,69 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     dv[qt] = ok ? a.dvec[(size_t)bh * N + row] : 0.f;
   }
 
-  // bf16 only: rounding corrections (see below). pkc accumulates sum_j P^blk_j c_j, the
-  // attention-weighted block centres; tpart the lane's share of sum_k dS_k.
-  constexpr bool kCorr = sizeof(T) == 2;
   f32x4 acc[DT][QT], pkc[DT][QT];
   float tpart[QT];
+  // correction weights: wr / wp hold the last eight blocks' sum_k r_k / P^blk (bf16, the
+  // newest in element 7); every four blocks the newest four move into the batch operands
+  // Wr / Wp at the slots of their C rows.
+  u32x4 wr[QT], wp[QT], Wr[QT], Wp[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     tpart[qt] = 0.f;
+    wr[qt] = wp[qt] = Wr[qt] = Wp[qt] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       acc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
       pkc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  // ones in row 0 of a 16 x 32 A operand: C row 0 = the column sums of B
+  F ones = E::zero();
+  if constexpr (kCorr) {
+    if (c16 == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
+  }
+
+  auto shift_in = [&](u32x4& r, float x) {  // drop element 0, append bf16(x) as element 7
+    const unsigned b = __builtin_bit_cast(unsigned short, (bf16)x);
+    r = u32x4{__builtin_amdgcn_alignbit(r[1], r[0], 16), __builtin_amdgcn_alignbit(r[2], r[1], 16),
+              __builtin_amdgcn_alignbit(r[3], r[2], 16), __builtin_amdgcn_alignbit(b, r[3], 16)};
+  };
+  // the four newest blocks are batch rows 4 qd .. 4 qd + 3, qd = (t % 32) / 4: A slots
+  // 0..3 of lane group qd (qd < 4) or slots 4..7 of group qd - 4 (qd >= 4)
+  auto commit = [&](int t) {
+    const int qd = (t & 31) >> 2;
+    if (g == (qd & 3)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        if (qd < 4) {
+          Wr[qt][0] = wr[qt][2]; Wr[qt][1] = wr[qt][3];
+          Wp[qt][0] = wp[qt][2]; Wp[qt][1] = wp[qt][3];
+        } else {
+          Wr[qt][2] = wr[qt][2]; Wr[qt][3] = wr[qt][3];
+          Wp[qt][2] = wp[qt][2]; Wp[qt][3] = wp[qt][3];
+        }
+      }
+    }
+  };
+  auto flush = [&](const char* cmb) {
+    if constexpr (kCorr) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      F ca;
+      CM::read_col4(cmb, 0, dt * 16, ca, 0);
+      CM::read_col4(cmb, 16, dt * 16, ca, 1);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        acc[dt][qt] = E::mma(ca, __builtin_bit_cast(F, Wr[qt]), acc[dt][qt]);
+        pkc[dt][qt] = E::mma(ca, __builtin_bit_cast(F, Wp[qt]), pkc[dt][qt]);
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) Wr[qt] = Wp[qt] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
 
   auto block = [&](int t, const char* stage, char* next) {
     const int j = block_of(t);
@@ -155,6 +230,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     if (t + 1 < cnt) issue(next, jn);
     const char* Kb = stage;
     const char* Vb = stage + KV::kBytes;
+    if constexpr (kCorr) {
+      // the previous batch's C rows are now visible to every wave
+      if ((t & 31) == 0 && t > 0) flush(((t >> 5) & 1) ? cm0 : cm1);
+      // row t % 32 of this batch's C: the block's first key row
+      if (w == 0 && l < 16) {
+        char* cmw = ((t >> 5) & 1) ? cm1 : cm0;
+        CM::store_chunk(cmw, t & 31, l, *reinterpret_cast<const u32x4*>(Kb + KV::offset(0, l * 8)));
+      }
+    }
 
     f32x4 s[4][QT], dp[4][QT];
 #pragma unroll
@@ -177,33 +261,45 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    const bool tail = (j + 1) * BKV > N;
-    float pblk[QT];
+    // keys past N exist only in the last, partial key block: P = 0 there
+    if ((j + 1) * BKV > N) {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) pblk[qt] = 0.f;
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j * BKV + kt * 16 + 4 * g + e >= N)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) s[kt][qt][e] = -INFINITY;
+    }
+    float pb[QT], tb[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) pb[qt] = tb[qt] = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool valid = !tail || (j * BKV + kt * 16 + 4 * g + e < N);
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const float p =
-              valid ? __builtin_amdgcn_exp2f(s[kt][qt][e] * a.scale_log2 - lse2[qt]) : 0.f;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][e], a.scale_log2, -lse2[qt]));
           const float ds = p * (dp[kt][qt][e] - dv[qt]);
           s[kt][qt][e] = ds;  // dS^T
           if (kCorr) {
-            pblk[qt] += p;
-            tpart[qt] += ds;
+            pb[qt] += p;
+            tb[qt] += ds;
           }
         }
-      }
 
+    f32x4 cs[QT];  // row 0: sum_k bf16(dS_k) of this block, per query column
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) cs[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       F pf[QT];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) pf[qt] = E::pack(s[2 * u][qt], s[2 * u + 1][qt]);
+      for (int qt = 0; qt < QT; ++qt) {
+        pf[qt] = E::pack(s[2 * u][qt], s[2 * u + 1][qt]);
+        if (kCorr) cs[qt] = E::mma(ones, pf[qt], cs[qt]);
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         F kt_;
@@ -214,37 +310,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       }
     }
     if constexpr (kCorr) {
-      // Two bf16 error terms grow with a large offset c_j shared by a block's keys (an
-      // attention-sink block), because each is multiplied by the keys:
-      //  * rounding dS to bf16 leaves sum_k r_k K_k, r = dS - bf16(dS), whose offset part
-      //    (sum_k r_k) c_j is added back here;
-      //  * the row term Dv carries the rounding of O, which shifts every dS_k by
-      //    -P_k dDv. In exact arithmetic sum_k dS_k = 0 over the row, so the measured
-      //    T = sum_k dS_k equals -dDv, and the shift's offset part, T sum_j P^blk_j c_j
-      //    (P^blk_j = the row's mass on block j), is removed in the epilogue.
-      // c_j = the block's first key row; what remains involves only K_k - c_j.
-      float rsum[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        float r = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r += s[kt][qt][e] - (float)(bf16)s[kt][qt][e];
-        rsum[qt] = sum4(r);
-        pblk[qt] = sum4(pblk[qt]);
+        tpart[qt] += tb[qt];
+        // cs row 0 lives in lanes of group 0, element 0; the other groups hold zeros
+        const float bsum = sum4(g == 0 ? cs[qt][0] : 0.f);
+        shift_in(wr[qt], sum4(tb[qt]) - bsum);
+        shift_in(wp[qt], sum4(pb[qt]));
       }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 c4 = *reinterpret_cast<const bf16x4*>(Kb + KV::offset(0, dt * 16 + 4 * g));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[dt][qt][e] += (float)c4[e] * rsum[qt];
-            pkc[dt][qt][e] += (float)c4[e] * pblk[qt];
-          }
-      }
+      if ((t & 3) == 3) commit(t);
     }
   };
   for (int t = 0; t < cnt; t += 2) {
@@ -253,6 +327,21 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   }
 
   if constexpr (kCorr) {
+    if (cnt > 0) {
+      // complete the last quad with zero weights, then apply the last batch
+      const int last = cnt - 1;
+      if ((last & 3) != 3) {
+        for (int t = last + 1; (t & 3) != 0; ++t)
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            shift_in(wr[qt], 0.f);
+            shift_in(wp[qt], 0.f);
+          }
+        commit(last | 3);
+      }
+      __syncthreads();  // the last C row written is visible
+      flush(((last >> 5) & 1) ? cm1 : cm0);
+    }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float tsum = sum4(tpart[qt]);
@@ -302,7 +391,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   using QTile = Tile<T, BQ, D>;
-  constexpr int kStage = 2 * QTile::kBytes;  // Q_i and dO_i
+  // A stage holds Q_i, dO_i and the statistics of its rows (LSE_i, then Dv_i, fp32), all
+  // streamed in by direct-to-LDS loads one block ahead.
+  constexpr int kStats = 2 * BQ * 4;
+  constexpr int kStage = 2 * QTile::kBytes + kStats;
   constexpr int NS = 2 * kStage <= 160 * 1024 ? 2 : 1;  // one stage only if two do not fit
   __shared__ __attribute__((aligned(1024))) char stage0[kStage];
   __shared__ __attribute__((aligned(1024))) char stage1[NS == 2 ? kStage : 16];
@@ -333,6 +425,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   auto issue = [&](char* stage, int i) {
     plan.issue_any(stage, Q, i * BQ, N, w);
     plan.issue_any(stage + QTile::kBytes, dO, i * BQ, N, w);
+    // statistics: 2 BQ floats, 64 per load (4 bytes per lane), wave w issues load w;
+    // rows past N are clamped here and given P = 0 in compute()
+    if (w < 2 * BQ / 64) {
+      const int e = w * 64 + l;
+      const int r = min(i * BQ + (e % BQ), N - 1);
+      const float* src = (e < BQ ? LSE : DV) + r;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (SPA2_LDS void*)(stage + 2 * QTile::kBytes + w * 256), 4, 0, 0);
+    }
   };
   if (cnt > 0) issue(stage0, block_of(0));
 
@@ -361,20 +462,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   auto compute = [&](int i, const char* stage) {
     const char* Qb = stage;
     const char* Db = stage + QTile::kBytes;
+    const char* St = stage + 2 * QTile::kBytes;
     // this lane's rows of the statistics: queries i*BQ + qrow0 + 16 mt + 4 g + e
     f32x4 l4[MT], d4[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int r = i * BQ + qrow0 + mt * 16 + 4 * g;
-      if (r + 3 < N && ((reinterpret_cast<uintptr_t>(LSE + r) | reinterpret_cast<uintptr_t>(DV + r)) & 15) == 0) {
-        l4[mt] = *reinterpret_cast<const f32x4*>(LSE + r);
-        d4[mt] = *reinterpret_cast<const f32x4*>(DV + r);
-      } else {
+      const int rl = qrow0 + mt * 16 + 4 * g;  // row within the block
+      l4[mt] = *reinterpret_cast<const f32x4*>(St + rl * 4);
+      d4[mt] = *reinterpret_cast<const f32x4*>(St + (BQ + rl) * 4);
+      if ((i + 1) * BQ > N) {  // last, partial query block: rows past N get P = 0
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          l4[mt][e] = r + e < N ? LSE[r + e] : INFINITY;  // rows past N get P = 0
-          d4[mt][e] = r + e < N ? DV[r + e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e)
+          if (i * BQ + rl + e >= N) {
+            l4[mt][e] = INFINITY;
+            d4[mt][e] = 0.f;
+          }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) l4[mt][e] *= kLog2e;
