@@ -105,9 +105,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   using KV = Tile<T, BKV, D>;
   constexpr bool kCorr = sizeof(T) == 2;
   using CM = Tile<T, 32, D>;  // c_j of one batch of 32 blocks (bf16 only)
-  // two stages in two LDS variables, named statically (see the forward kernel)
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * KV::kBytes];
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * KV::kBytes];
+  // K/V stages in separate LDS variables, named statically (see the forward kernel): three
+  // (loads issued two blocks ahead) when they fit next to C, else two
+  constexpr int kStageBytes = 2 * KV::kBytes;
+  constexpr int NS = kCorr && 3 * kStageBytes + 2 * CM::kBytes <= 160 * 1024 ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char stage1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char stage2[NS == 3 ? kStageBytes : 16];
   __shared__ __attribute__((aligned(1024))) char cm0[kCorr ? CM::kBytes : 16];
   __shared__ __attribute__((aligned(1024))) char cm1[kCorr ? CM::kBytes : 16];
 
@@ -134,7 +138,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     plan.issue_any(stage, K, j * BKV, N, w);
     plan.issue_any(stage + KV::kBytes, V, j * BKV, N, w);
   };
-  if (cnt > 0) issue(stage0, block_of(0));
+  // block indices of the next NS - 1 blocks (the list cursor only moves forward)
+  int jf[NS - 1];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) jf[i] = i < cnt ? block_of(i) : 0;
+  if (cnt > 0) issue(stage0, jf[0]);
+  if (NS == 3 && cnt > 1) issue(stage1, jf[NS - 2]);
   if constexpr (kCorr) {  // C starts at zero: unfilled rows meet zero weights
     const u32x4 z{0u, 0u, 0u, 0u};
     for (int o = tid * 16; o < CM::kBytes; o += 256 * 16) {
@@ -222,12 +231,22 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
+  // Per-wave direct-to-LDS loads of one block (K and V), for the partial waits below.
+  constexpr int kBlockLoads = 2 * KV::template Plan<4>::kLoads;
+  // block t: its stage is `stage`; the loads of block t + NS - 1 go to `next`
   auto block = [&](int t, const char* stage, char* next) {
-    const int j = block_of(t);
-    const int jn = t + 1 < cnt ? block_of(t + 1) : 0;
-    wait_vmem();      // this wave's loads of block t have landed
+    const int j = jf[0];
+    const int ahead = t + NS - 1;
+    const int jn = ahead < cnt ? block_of(ahead) : 0;
+#pragma unroll
+    for (int i = 0; i < NS - 2; ++i) jf[i] = jf[i + 1];
+    jf[NS - 2] = jn;
+    // this wave's loads of block t have landed: with three stages the loads of block
+    // t + 1 (issued later; loads complete in order) may still be in flight
+    if (NS == 3 && t + 1 < cnt) wait_vmem_below<kBlockLoads>();
+    else wait_vmem();
     __syncthreads();  // ... and every other wave's; block t-1 is no longer being read
-    if (t + 1 < cnt) issue(next, jn);
+    if (ahead < cnt) issue(next, jn);
     const char* Kb = stage;
     const char* Vb = stage + KV::kBytes;
     if constexpr (kCorr) {
@@ -321,9 +340,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       if ((t & 3) == 3) commit(t);
     }
   };
-  for (int t = 0; t < cnt; t += 2) {
-    block(t, stage0, stage1);
-    if (t + 1 < cnt) block(t + 1, stage1, stage0);
+  if constexpr (NS == 3) {
+    for (int t = 0; t < cnt; t += 3) {
+      block(t, stage0, stage2);
+      if (t + 1 < cnt) block(t + 1, stage1, stage0);
+      if (t + 2 < cnt) block(t + 2, stage2, stage1);
+    }
+  } else {
+    for (int t = 0; t < cnt; t += 2) {
+      block(t, stage0, stage1);
+      if (t + 1 < cnt) block(t + 1, stage1, stage0);
+    }
   }
 
   if constexpr (kCorr) {

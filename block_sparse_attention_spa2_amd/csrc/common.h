@@ -89,6 +89,13 @@ struct ListCursor {
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained): this wave's outstanding
 // vector memory operations, including direct-to-LDS loads, have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0xF70); }
+// s_waitcnt vmcnt(N): at most the N most recent vector memory operations of this wave are
+// still outstanding (loads complete in issue order), so everything issued earlier is done.
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // ------------------------------------------------------------------------------------
 // Element traits: fragment type, MFMA step, conversions.
