@@ -129,21 +129,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
   constexpr bool dense = DENSE;
   const int cnt = dense ? a.Tn : a.row_cnt[item];
-  ListCursor cur;
-  if (!dense) cur.init(a.row_idx + (size_t)item * a.Tn, cnt);
-  auto block_of = [&](int t) { return dense ? t : cur.at(t); };
+  BlockQueue<NS> bq;  // blocks t .. t + NS - 1 (tile loads) and t + NS (being read)
+  if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, cnt);
+  auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
   typename KV::template Plan<4> plan;
   plan.init(w);
   auto issue = [&](char* stage, int j) {
     plan.issue_any(stage, K, j * BKV, N, w);
     plan.issue_any(stage + KV::kBytes, V, j * BKV, N, w);
   };
-  // block indices of the next NS - 1 blocks (the list cursor only moves forward)
-  int jf[NS - 1];
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i) jf[i] = i < cnt ? block_of(i) : 0;
-  if (cnt > 0) issue(stage0, jf[0]);
-  if (NS == 3 && cnt > 1) issue(stage1, jf[NS - 2]);
+  if (cnt > 0) issue(stage0, block_at(0, 0));
+  if (NS == 3 && cnt > 1) issue(stage1, block_at(0, 1));
   if constexpr (kCorr) {  // C starts at zero: unfilled rows meet zero weights
     const u32x4 z{0u, 0u, 0u, 0u};
     for (int o = tid * 16; o < CM::kBytes; o += 256 * 16) {
@@ -235,17 +231,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int kBlockLoads = 2 * KV::template Plan<4>::kLoads;
   // block t: its stage is `stage`; the loads of block t + NS - 1 go to `next`
   auto block = [&](int t, const char* stage, char* next) {
-    const int j = jf[0];
+    const int j = block_at(t, 0);
     const int ahead = t + NS - 1;
-    const int jn = ahead < cnt ? block_of(ahead) : 0;
-#pragma unroll
-    for (int i = 0; i < NS - 2; ++i) jf[i] = jf[i + 1];
-    jf[NS - 2] = jn;
+    const int jn = block_at(t, NS - 1);
+    if (!dense) bq.advance(t);
     // this wave's loads of block t have landed: with three stages the loads of block
     // t + 1 (issued later; loads complete in order) may still be in flight
     if (NS == 3 && t + 1 < cnt) wait_vmem_below<kBlockLoads>();
     else wait_vmem();
-    __syncthreads();  // ... and every other wave's; block t-1 is no longer being read
+    lds_barrier();  // ... and every other wave's; block t-1 is no longer being read
     if (ahead < cnt) issue(next, jn);
     const char* Kb = stage;
     const char* Vb = stage + KV::kBytes;
@@ -444,9 +438,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   constexpr bool dense = DENSE;
   const int cnt = dense ? a.Tm : a.col_cnt[item];
-  ListCursor cur;
-  if (!dense) cur.init(a.col_idx + (size_t)item * a.Tm, cnt);
-  auto block_of = [&](int t) { return dense ? t : cur.at(t); };
+  BlockQueue<2> bq;  // query blocks t, t + 1 (next tile load) and t + 2 (being read)
+  if (!dense) bq.init(a.col_idx + (size_t)item * a.Tm, cnt);
+  auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
   typename QTile::template Plan<4> plan;
   plan.init(w);
   auto issue = [&](char* stage, int i) {
@@ -462,7 +456,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                                        (SPA2_LDS void*)(stage + 2 * QTile::kBytes + w * 256), 4, 0, 0);
     }
   };
-  if (cnt > 0) issue(stage0, block_of(0));
+  if (cnt > 0) issue(stage0, block_at(0, 0));
 
   // K, V as B operands: lane -> key k0 + 16 kt + c16, dims 32 ks + 8 g .. +8
   F kf[KT][KS], vf[KT][KS];
@@ -568,10 +562,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   if constexpr (NS == 2) {
     auto block = [&](int t, const char* stage, char* next) {
-      const int i = block_of(t);
-      const int in = t + 1 < cnt ? block_of(t + 1) : 0;
+      const int i = block_at(t, 0);
+      const int in = block_at(t, 1);
+      if (!dense) bq.advance(t);
       wait_vmem();
-      __syncthreads();
+      lds_barrier();
       if (t + 1 < cnt) issue(next, in);
       compute(i, stage);
     };
@@ -581,12 +576,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     }
   } else {
     for (int t = 0; t < cnt; ++t) {
-      const int i = block_of(t);
-      const int in = t + 1 < cnt ? block_of(t + 1) : 0;
+      const int i = block_at(t, 0);
+      const int in = block_at(t, 1);
+      if (!dense) bq.advance(t);
       wait_vmem();
-      __syncthreads();
+      lds_barrier();
       compute(i, stage0);
-      __syncthreads();  // every wave is done with the only stage
+      lds_barrier();  // every wave is done with the only stage
       if (t + 1 < cnt) issue(stage0, in);
     }
   }

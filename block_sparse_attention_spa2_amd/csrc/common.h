@@ -63,32 +63,45 @@ __device__ __forceinline__ int xcd_item(int bid, int items) {
   return x * q + min(x, r) + slot;
 }
 
-// A block list read 64 entries at a time into one VGPR (entry i in lane i % 64), so the
-// index of block t is a v_readlane instead of a memory load inside the main loop.
-struct ListCursor {
-  const int32_t* list;
+// The kept-block list of one work item, read ahead with scalar loads. The lists are not
+// written while a kernel runs, so they are read through the constant address space: the
+// wait for an entry is an lgkmcnt wait, never a wait for the direct-to-LDS tile loads in
+// flight (a vector load of the entry would complete only after those, since vector memory
+// operations complete in issue order). q[i] is the block at position t + i of the list
+// (i <= AHEAD; 0 past the end); advance() moves from t to t + 1 and starts reading the
+// entry AHEAD + 1 positions ahead. t must be wave-uniform.
+template <int AHEAD>
+struct BlockQueue {
+  const __attribute__((address_space(4))) int32_t* list;
   int cnt;
-  int held;  // entries [base, base + 64) of the list, one per lane
-  int base;
-  __device__ __forceinline__ void init(const int32_t* l_, int cnt_) {
-    list = l_;
+  int q[AHEAD + 1];
+  __device__ __forceinline__ void init(const int32_t* l, int cnt_) {
+    list = (const __attribute__((address_space(4))) int32_t*)l;
     cnt = cnt_;
-    base = 0;
-    held = lane_id() < cnt ? list[lane_id()] : 0;
+#pragma unroll
+    for (int i = 0; i <= AHEAD; ++i) q[i] = i < cnt ? list[i] : 0;
   }
-  // t must be wave-uniform and visited in increasing order
-  __device__ __forceinline__ int at(int t) {
-    if (t - base >= 64) {
-      base += 64;
-      held = base + lane_id() < cnt ? list[base + lane_id()] : 0;
-    }
-    return __builtin_amdgcn_readlane(held, t - base);
+  __device__ __forceinline__ void advance(int t) {
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) q[i] = q[i + 1];
+    const int n = t + 1 + AHEAD;
+    q[AHEAD] = n < cnt ? list[n] : 0;
   }
 };
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained): this wave's outstanding
 // vector memory operations, including direct-to-LDS loads, have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0xF70); }
+// Workgroup barrier for LDS tiles filled by direct-to-LDS loads. __syncthreads() (and a
+// workgroup fence on LDS) makes every wave wait for all of its outstanding direct-to-LDS
+// loads, including those issued ahead for later blocks; here the caller first waits for
+// the loads it needs (vmcnt), this wave's own LDS accesses are completed (lgkmcnt(0)),
+// and the barrier is an s_barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // s_waitcnt vmcnt(N): at most the N most recent vector memory operations of this wave are
 // still outstanding (loads complete in issue order), so everything issued earlier is done.
 template <int N>

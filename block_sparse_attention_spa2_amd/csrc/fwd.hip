@@ -68,16 +68,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   constexpr bool dense = DENSE;  // dense: every key block, no list
   const int cnt = dense ? a.Tn : a.row_cnt[item];
-  ListCursor cur;
-  if (!dense) cur.init(a.row_idx + (size_t)item * a.Tn, cnt);
-  auto block_of = [&](int t) { return dense ? t : cur.at(t); };
+  BlockQueue<2> bq;  // blocks t, t + 1 (next tile load) and t + 2 (being read)
+  if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, cnt);
+  auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
   typename KV::template Plan<4> plan;
   plan.init(w);
   auto issue = [&](char* stage, int j) {
     plan.issue_any(stage, K, j * BKV, N, w);
     plan.issue_any(stage + KV::kBytes, V, j * BKV, N, w);
   };
-  if (cnt > 0) issue(stage0, block_of(0));
+  if (cnt > 0) issue(stage0, block_at(0, 0));
 
   // Q as the B operand: lane -> query q0 + 16 qt + c16, dims 32 ks + 8 g .. +8
   F qf[QT][KS];
@@ -102,10 +102,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 
   auto block = [&](int t, const char* stage, char* next) {
-    const int j = block_of(t);
-    const int jn = t + 1 < cnt ? block_of(t + 1) : 0;
+    const int j = block_at(t, 0);
+    const int jn = block_at(t, 1);
+    if (!dense) bq.advance(t);
     wait_vmem();      // this wave's loads of block t have landed
-    __syncthreads();  // ... and every other wave's; block t-1 is no longer being read
+    lds_barrier();  // ... and every other wave's; block t-1 is no longer being read
     if (t + 1 < cnt) issue(next, jn);
     const char* Kb = stage;
     const char* Vb = stage + KV::kBytes;
