@@ -393,22 +393,26 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------------
 // dK, dV: per key block, over the query blocks that keep it (column lists).
-// Wave w owns key half kh = w % 2 (32 keys) and query half qh = w / 2 of every query
-// block, so each wave reads only its half of Q_i and dO_i from LDS (in both layouts),
-// which halves the LDS traffic per matrix instruction compared with 16 keys per wave
-// over all rows. Q_i and dO_i stream into LDS with global_load_lds, one block ahead;
-// LSE and Dv of the wave's rows are read straight from global memory.
+// NW waves split each (key block, query block) pair into KW key groups of 16 KT keys
+// times QW = NW / KW query groups, so each wave reads only its rows of Q_i and dO_i from
+// LDS (in both layouts). Eight waves (16 keys each, two waves per SIMD) keep the register
+// footprint of a wave small enough for two of them to share a SIMD; four waves (32 keys
+// each) halve the LDS traffic per matrix instruction instead. Q_i, dO_i and the row
+// statistics stream into LDS with global_load_lds, one block ahead.
 //   S = Q K^T, dP = dO V^T (A = Q, dO rows from LDS; B = K, V in registers),
 //   dS = P * (dP - Dv), dV^T += dO^T P, dK^T += Q^T dS (A via transpose reads).
-// At the end the two query halves' partial sums are added through LDS.
+// At the end the query groups' partial sums are added through LDS.
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int BQ, bool DENSE>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+template <typename T, int D, int BQ, bool DENSE, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BKV = 64;
-  constexpr int MT = BQ / 32;  // 16-row query tiles per wave (half of the query block)
-  constexpr int KT = 2;        // 16-key tiles per wave (32 keys)
+  constexpr int KT = NW == 8 ? 1 : 2;    // 16-key tiles per wave
+  constexpr int KW = BKV / (16 * KT);    // key groups
+  constexpr int QW = NW / KW;            // query groups
+  static_assert(QW == 2, "the final reduction adds two query groups");
+  constexpr int MT = BQ / QW / 16;       // 16-row query tiles per wave
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   using QTile = Tile<T, BQ, D>;
@@ -422,7 +426,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = w & 1, qh = w >> 1;
+  const int kh = w % KW, qh = w / KW;
   const int item = xcd_item(blockIdx.x, a.BH * a.Tn);
   const int bh = item / a.Tn, kb = item % a.Tn;
   const int N = a.N;
@@ -433,15 +437,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const T* dO = (const T*)a.dout + head;
   const float* LSE = a.lse + (size_t)bh * N;
   const float* DV = a.dvec + (size_t)bh * N;
-  const int k0 = kb * BKV + kh * 32;  // first key of this wave
-  const int qrow0 = qh * (BQ / 2);    // first query row of this wave within a query block
+  const int k0 = kb * BKV + kh * 16 * KT;  // first key of this wave
+  const int qrow0 = qh * (BQ / QW);        // first query row of this wave within a block
 
   constexpr bool dense = DENSE;
   const int cnt = dense ? a.Tm : a.col_cnt[item];
   BlockQueue<2> bq;  // query blocks t, t + 1 (next tile load) and t + 2 (being read)
   if (!dense) bq.init(a.col_idx + (size_t)item * a.Tm, cnt);
   auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
-  typename QTile::template Plan<4> plan;
+  typename QTile::template Plan<NW> plan;
   plan.init(w);
   auto issue = [&](char* stage, int i) {
     plan.issue_any(stage, Q, i * BQ, N, w);
@@ -653,8 +657,9 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
   do {                                                                           \
     if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);        \
     if (stages & kBwdDkdv) {                                                     \
-      if (m) bwd_dkdv_kernel<T, D, BQ, false><<<gk, 256, 0, st>>>(a);           \
-      else bwd_dkdv_kernel<T, D, BQ, true><<<gk, 256, 0, st>>>(a);              \
+      constexpr int nw = sizeof(T) == 2 ? 8 : 4;                                 \
+      if (m) bwd_dkdv_kernel<T, D, BQ, false, nw><<<gk, 64 * nw, 0, st>>>(a);   \
+      else bwd_dkdv_kernel<T, D, BQ, true, nw><<<gk, 64 * nw, 0, st>>>(a);      \
     }                                                                            \
     if (stages & kBwdDq) {                                                       \
       if (m) bwd_dq_kernel<T, D, BQ, false><<<gq, 256, 0, st>>>(a);             \
