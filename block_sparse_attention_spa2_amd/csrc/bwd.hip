@@ -94,12 +94,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // every 32 blocks acc += C^T W, pkc += C^T W'. sum_k bf16(dS_k) comes from the matrix unit
 // too (a ones operand times the packed dS), so sum_k r_k costs one add per element.
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int BQ, bool DENSE>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+template <typename T, int D, int BQ, bool DENSE, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BKV = 64;
-  constexpr int QT = BQ / 64;
+  constexpr int QT = BQ / (16 * NW);  // 16-row query tiles per wave
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   using KV = Tile<T, BKV, D>;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   BlockQueue<NS> bq;  // blocks t .. t + NS - 1 (tile loads) and t + NS (being read)
   if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, cnt);
   auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
-  typename KV::template Plan<4> plan;
+  typename KV::template Plan<NW> plan;
   plan.init(w);
   auto issue = [&](char* stage, int j) {
     plan.issue_any(stage, K, j * BKV, N, w);
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   if (NS == 3 && cnt > 1) issue(stage1, block_at(0, 1));
   if constexpr (kCorr) {  // C starts at zero: unfilled rows meet zero weights
     const u32x4 z{0u, 0u, 0u, 0u};
-    for (int o = tid * 16; o < CM::kBytes; o += 256 * 16) {
+    for (int o = tid * 16; o < CM::kBytes; o += 64 * NW * 16) {
       *reinterpret_cast<u32x4*>(cm0 + o) = z;
       *reinterpret_cast<u32x4*>(cm1 + o) = z;
     }
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   };
 
   // Per-wave direct-to-LDS loads of one block (K and V), for the partial waits below.
-  constexpr int kBlockLoads = 2 * KV::template Plan<4>::kLoads;
+  constexpr int kBlockLoads = 2 * KV::template Plan<NW>::kLoads;
   // block t: its stage is `stage`; the loads of block t + NS - 1 go to `next`
   auto block = [&](int t, const char* stage, char* next) {
     const int j = block_at(t, 0);
@@ -662,8 +662,9 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
       else bwd_dkdv_kernel<T, D, BQ, true, nw><<<gk, 64 * nw, 0, st>>>(a);      \
     }                                                                            \
     if (stages & kBwdDq) {                                                       \
-      if (m) bwd_dq_kernel<T, D, BQ, false><<<gq, 256, 0, st>>>(a);             \
-      else bwd_dq_kernel<T, D, BQ, true><<<gq, 256, 0, st>>>(a);                \
+      constexpr int nq = sizeof(T) == 2 ? BQ / 16 : 4;                          \
+      if (m) bwd_dq_kernel<T, D, BQ, false, nq><<<gq, 64 * nq, 0, st>>>(a);     \
+      else bwd_dq_kernel<T, D, BQ, true, nq><<<gq, 64 * nq, 0, st>>>(a);        \
     }                                                                            \
   } while (0)
   if (s.dtype == SPA2_BF16) {
