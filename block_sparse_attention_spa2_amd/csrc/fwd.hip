@@ -40,12 +40,12 @@ struct FwdArgs {
 // Rescale threshold in log2 units: probabilities stay below 2^8 between rescales.
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int D, int BQ, bool DENSE>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+template <typename T, int D, int BQ, bool DENSE, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BKV = 64;
-  constexpr int QT = BQ / 64;  // 16-row query tiles per wave
+  constexpr int QT = BQ / (16 * NW);  // 16-row query tiles per wave
   constexpr int KS = D / 32;   // reduction steps over the head dimension
   constexpr int DT = D / 16;   // 16-wide output column tiles
   using KV = Tile<T, BKV, D>;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   BlockQueue<2> bq;  // blocks t, t + 1 (next tile load) and t + 2 (being read)
   if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, cnt);
   auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
-  typename KV::template Plan<4> plan;
+  typename KV::template Plan<NW> plan;
   plan.init(w);
   auto issue = [&](char* stage, int j) {
     plan.issue_any(stage, K, j * BKV, N, w);
@@ -216,6 +216,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// Waves per workgroup. Four (32 query rows each for 128-row blocks, two workgroups and so
+// two waves per SIMD) measured faster than eight waves of 16 rows (four per SIMD), which
+// read every K/V tile from LDS twice as often per matrix instruction.
+template <typename T, int BQ>
+constexpr int fwd_waves() { return 4; }
+
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const int32_t* row_cnt, const int32_t* row_idx, void* o, float* lse,
                       float* o_f32, hipStream_t st) {
@@ -224,8 +230,9 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
   const dim3 grid(s.BH() * s.Tm);
 #define SPA2_FWD(T, D, BQ)                                               \
   do {                                                                   \
-    if (row_cnt) fwd_kernel<T, D, BQ, false><<<grid, 256, 0, st>>>(a);   \
-    else fwd_kernel<T, D, BQ, true><<<grid, 256, 0, st>>>(a);            \
+    constexpr int nw = fwd_waves<T, BQ>();                               \
+    if (row_cnt) fwd_kernel<T, D, BQ, false, nw><<<grid, 64 * nw, 0, st>>>(a); \
+    else fwd_kernel<T, D, BQ, true, nw><<<grid, 64 * nw, 0, st>>>(a);    \
   } while (0)
   if (s.dtype == SPA2_BF16) {
     if (s.D == 64) {
