@@ -403,16 +403,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 //   dS = P * (dP - Dv), dV^T += dO^T P, dK^T += Q^T dS (A via transpose reads).
 // At the end the query groups' partial sums are added through LDS.
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int BQ, bool DENSE, int NW>
+template <typename T, int D, int BQ, bool DENSE, int NW, int KT>
 __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BKV = 64;
-  constexpr int KT = NW == 8 ? 1 : 2;    // 16-key tiles per wave
-  constexpr int KW = BKV / (16 * KT);    // key groups
+  constexpr int KW = BKV / (16 * KT);    // key groups (KT 16-key tiles per wave)
   constexpr int QW = NW / KW;            // query groups
-  static_assert(QW == 2, "the final reduction adds two query groups");
   constexpr int MT = BQ / QW / 16;       // 16-row query tiles per wave
+  static_assert(MT % 2 == 0, "the dV/dK products reduce over 32 query rows at a time");
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   using QTile = Tile<T, BQ, D>;
@@ -591,23 +590,26 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // add the query halves: waves with qh = 1 hand their partial sums to qh = 0 via LDS,
-  // one tensor at a time (DT * KT * 1 KB per wave)
+  // add the query groups: waves with qh = r > 0 hand their partial sums to qh = 0 via
+  // LDS, one group and one tensor at a time (DT * KT * 1 KB per wave)
   f32x4* xfer = reinterpret_cast<f32x4*>(stage0);
   auto reduce = [&](f32x4 (&acc)[DT][KT]) {
-    __syncthreads();
-    if (qh == 1) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int r = 1; r < QW; ++r) {
+      __syncthreads();
+      if (qh == r) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) xfer[((kh * DT + dt) * KT + kt) * 64 + l] = acc[dt][kt];
-    }
-    __syncthreads();
-    if (qh == 0) {
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+          for (int kt = 0; kt < KT; ++kt) xfer[((kh * DT + dt) * KT + kt) * 64 + l] = acc[dt][kt];
+      }
+      __syncthreads();
+      if (qh == 0) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) acc[dt][kt] += xfer[((kh * DT + dt) * KT + kt) * 64 + l];
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) acc[dt][kt] += xfer[((kh * DT + dt) * KT + kt) * 64 + l];
+      }
     }
   };
   reduce(dk);
@@ -640,6 +642,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// dK/dV work split: bf16 runs eight waves per workgroup (two per SIMD) of one 16-key tile
+// each (32 keys per wave would need more than the 256 registers of two waves per SIMD);
+// fp32 runs four waves of two tiles.
+template <typename T, int BQ>
+constexpr int dkdv_key_tiles() { return sizeof(T) == 2 ? 1 : 2; }
+
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* o_f32, const float* lse, const void* dout, const spa2_blockmask* m, void* dq,
                       void* dk, void* dv, float* dvec, int stages, hipStream_t st) {
@@ -657,9 +665,9 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
   do {                                                                           \
     if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);        \
     if (stages & kBwdDkdv) {                                                     \
-      constexpr int nw = sizeof(T) == 2 ? 8 : 4;                                 \
-      if (m) bwd_dkdv_kernel<T, D, BQ, false, nw><<<gk, 64 * nw, 0, st>>>(a);   \
-      else bwd_dkdv_kernel<T, D, BQ, true, nw><<<gk, 64 * nw, 0, st>>>(a);      \
+      constexpr int nw = sizeof(T) == 2 ? 8 : 4, kt = dkdv_key_tiles<T, BQ>(); \
+      if (m) bwd_dkdv_kernel<T, D, BQ, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+      else bwd_dkdv_kernel<T, D, BQ, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a);    \
     }                                                                            \
     if (stages & kBwdDq) {                                                       \
       constexpr int nq = sizeof(T) == 2 ? BQ / 16 : 4;                          \

@@ -196,22 +196,59 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     if (t + 1 < cnt) block(t + 1, stage1, stage0);
   }
 
-  // epilogue: normalise, store O rows and LSE
-  T* O = (T*)a.o + head;
+  // epilogue: normalise, then store O (and the unrounded copy) through LDS, so that every
+  // global store writes whole 16-byte chunks of consecutive columns of a row (full cache
+  // lines) instead of 4 columns of 16 rows. The fp32 tile (BQ x D) goes into the two
+  // stages, rows [0, BQ/2) into stage0 and the rest into stage1, with the 16-byte chunks
+  // of row r XOR-swizzled by r mod 32 (conflict-free writes of 16 rows at a time).
   float* lse = a.lse + (size_t)bh * N;
+  constexpr int kRowChunks = D / 4;               // 16-byte fp32 chunks per row
+  constexpr int kHalfRows = BQ / 2;
+  static_assert(kHalfRows * D * 4 <= 2 * KV::kBytes, "a stage holds half of the O tile");
+  auto chunk_at = [&](int r, int c) -> f32x4* {  // row r of the block, chunk c
+    char* base = r < kHalfRows ? stage0 : stage1;
+    const int rr = r % kHalfRows;
+    return reinterpret_cast<f32x4*>(base + rr * D * 4 + ((c ^ (rr & (kRowChunks - 1) & 31)) << 4));
+  };
+  lds_barrier();  // every wave is done with the K/V stages
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int row = q0 + qt * 16 + c16;
+    const int rl = w * 16 * QT + qt * 16 + c16;  // row within the block
+    const int row = qb * BQ + rl;
     const float lt = sum4(lrow[qt]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (row < N) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 of = oacc[dt][qt] * inv;
-        if (a.o_f32) store4_stream(a.o_f32 + head + (size_t)row * D + dt * 16 + 4 * g, of);
-        store4_stream(O + (size_t)row * D + dt * 16 + 4 * g, of);
+    for (int dt = 0; dt < DT; ++dt) *chunk_at(rl, dt * 4 + g) = oacc[dt][qt] * inv;
+    if (g == 0 && row < N) lse[row] = lt > 0.f ? (mrow[qt] + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+  lds_barrier();
+  const int rows_here = min(BQ, N - qb * BQ);
+  T* O = (T*)a.o + head + (size_t)qb * BQ * D;
+  constexpr int kEpc = 16 / (int)sizeof(T);        // elements per 16-byte output chunk
+  constexpr int kOutChunks = BQ * D / kEpc;
+  for (int f = tid; f < kOutChunks; f += 64 * NW) {
+    const int r = f / (D / kEpc), c = f % (D / kEpc);
+    if (r >= rows_here) break;  // chunks are in row order
+    if constexpr (sizeof(T) == 2) {
+      const f32x4 lo = *chunk_at(r, 2 * c), hi = *chunk_at(r, 2 * c + 1);
+      bf16x8 ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ob[e] = (bf16)lo[e];
+        ob[4 + e] = (bf16)hi[e];
       }
-      if (g == 0) lse[row] = lt > 0.f ? (mrow[qt] + __log2f(lt)) * kLn2 : -INFINITY;
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ob),
+                                  reinterpret_cast<u32x4*>(O + (size_t)r * D + c * kEpc));
+    } else {
+      __builtin_nontemporal_store(*chunk_at(r, c), reinterpret_cast<f32x4*>(O + (size_t)r * D + c * kEpc));
+    }
+  }
+  if (a.o_f32) {
+    float* Of = a.o_f32 + head + (size_t)qb * BQ * D;
+    for (int f = tid; f < BQ * kRowChunks; f += 64 * NW) {
+      const int r = f / kRowChunks, c = f % kRowChunks;
+      if (r >= rows_here) break;
+      __builtin_nontemporal_store(*chunk_at(r, c), reinterpret_cast<f32x4*>(Of + (size_t)r * D + c * 4));
     }
   }
 }
