@@ -54,6 +54,10 @@ def _check_bm(bm: "BlockMask", q: torch.Tensor) -> None:
     _expect("row_idx", bm.row_idx, (B, H, tm, tn), torch.int32)
     _expect("col_cnt", bm.col_cnt, (B, H, tn), torch.int32)
     _expect("col_idx", bm.col_idx, (B, H, tn, tm), torch.int32)
+    if bm.row_order is not None:
+        _expect("row_order", bm.row_order, (B, H, tm), torch.int32)
+    if bm.col_order is not None:
+        _expect("col_order", bm.col_order, (B, H, tn), torch.int32)
 
 
 def _ptr(t: torch.Tensor | None):
@@ -80,6 +84,8 @@ class BlockMask:
     col_idx: torch.Tensor   # int32 [B, H, Tn, Tm]
     bq: int
     bkv: int
+    row_order: torch.Tensor | None = None  # int32 [B, H, Tm], scheduling order (optional)
+    col_order: torch.Tensor | None = None  # int32 [B, H, Tn]
 
     @staticmethod
     def empty(B: int, H: int, N: int, bq: int, bkv: int, device) -> "BlockMask":
@@ -91,11 +97,14 @@ class BlockMask:
             row_idx=torch.empty((B, H, tm, tn), dtype=torch.int32, **kw),
             col_cnt=torch.empty((B, H, tn), dtype=torch.int32, **kw),
             col_idx=torch.empty((B, H, tn, tm), dtype=torch.int32, **kw),
-            bq=bq, bkv=bkv)
+            bq=bq, bkv=bkv,
+            row_order=torch.empty((B, H, tm), dtype=torch.int32, **kw),
+            col_order=torch.empty((B, H, tn), dtype=torch.int32, **kw))
 
     def c(self) -> _lib.BlockMaskC:
         return _lib.BlockMaskC(_ptr(self.mask), _ptr(self.row_cnt), _ptr(self.row_idx),
-                               _ptr(self.col_cnt), _ptr(self.col_idx))
+                               _ptr(self.col_cnt), _ptr(self.col_idx),
+                               _ptr(self.row_order), _ptr(self.col_order))
 
     def kept_fraction(self) -> float:
         return float(self.mask.float().mean())

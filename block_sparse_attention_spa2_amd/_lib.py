@@ -18,7 +18,8 @@ class Desc(C.Structure):
 
 class BlockMaskC(C.Structure):
     _fields_ = [("mask", C.c_void_p), ("row_cnt", C.c_void_p), ("row_idx", C.c_void_p),
-                ("col_cnt", C.c_void_p), ("col_idx", C.c_void_p)]
+                ("col_cnt", C.c_void_p), ("col_idx", C.c_void_p), ("row_order", C.c_void_p),
+                ("col_order", C.c_void_p)]
 
 
 # name -> (restype, argtypes)

@@ -65,6 +65,17 @@ spa2_status hip_status(const char* where, hipError_t e) {
   return SPA2_E_HIP;
 }
 
+// Lists are complete: write the scheduling orders the caller asked for.
+spa2_status write_orders(const spa2::Shape& s, const spa2_blockmask& m, hipStream_t hs) {
+  spa2_status st = SPA2_OK;
+  if (m.row_order &&
+      (st = hip_status("order", spa2::launch_order(m.row_cnt, s.BH() * s.Tm, s.Tn, m.row_order, hs))) != SPA2_OK)
+    return st;
+  if (m.col_order)
+    st = hip_status("order", spa2::launch_order(m.col_cnt, s.BH() * s.Tn, s.Tm, m.col_order, hs));
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,7 +140,8 @@ spa2_status spa2_mask(const spa2_desc* desc, const void* q, const void* k, doubl
                                                      topk_count(k_frac, s.Tn), p_frac, *out,
                                                      hs))) != SPA2_OK)
     return st;
-  return hip_status("cols", spa2::launch_cols(s, *out, hs));
+  if ((st = hip_status("cols", spa2::launch_cols(s, *out, hs))) != SPA2_OK) return st;
+  return write_orders(s, *out, hs);
 }
 
 spa2_status spa2_select(const spa2_desc* desc, const double* pbar, double k_frac, double p_frac,
@@ -145,7 +157,8 @@ spa2_status spa2_select(const spa2_desc* desc, const double* pbar, double k_frac
                                                      topk_count(k_frac, s.Tn), p_frac, *out,
                                                      hs))) != SPA2_OK)
     return st;
-  return hip_status("cols", spa2::launch_cols(s, *out, hs));
+  if ((st = hip_status("cols", spa2::launch_cols(s, *out, hs))) != SPA2_OK) return st;
+  return write_orders(s, *out, hs);
 }
 
 spa2_status spa2_mask_lists(const spa2_desc* desc, const spa2_blockmask* m, void* stream) {
@@ -155,7 +168,8 @@ spa2_status spa2_mask_lists(const spa2_desc* desc, const spa2_blockmask* m, void
   if ((st = check_blockmask(m, true)) != SPA2_OK) return st;
   const hipStream_t hs = (hipStream_t)stream;
   if ((st = hip_status("rows", spa2::launch_rows(s, *m, hs))) != SPA2_OK) return st;
-  return hip_status("cols", spa2::launch_cols(s, *m, hs));
+  if ((st = hip_status("cols", spa2::launch_cols(s, *m, hs))) != SPA2_OK) return st;
+  return write_orders(s, *m, hs);
 }
 
 spa2_status spa2_fwd(const spa2_desc* desc, const void* q, const void* k, const void* v,
@@ -167,8 +181,8 @@ spa2_status spa2_fwd(const spa2_desc* desc, const void* q, const void* k, const 
   if (!q || !k || !v || !o || !lse) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
   return hip_status("fwd", spa2::launch_fwd(s, q, k, v, m ? m->row_cnt : nullptr,
-                                            m ? m->row_idx : nullptr, o, lse, o_f32,
-                                            (hipStream_t)stream));
+                                            m ? m->row_idx : nullptr, m ? m->row_order : nullptr,
+                                            o, lse, o_f32, (hipStream_t)stream));
 }
 
 spa2_status spa2_bwd_workspace_size(const spa2_desc* desc, size_t* bytes) {

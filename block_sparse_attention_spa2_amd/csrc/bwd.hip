@@ -34,6 +34,8 @@ struct BwdArgs {
   const int32_t* row_idx;
   const int32_t* col_cnt;
   const int32_t* col_idx;
+  const int32_t* row_order;  // optional scheduling orders (query blocks, key blocks)
+  const int32_t* col_order;
   void* dq;
   void* dk;
   void* dv;
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int item = xcd_item(blockIdx.x, a.BH * a.Tm);
+  const int pos = xcd_item(blockIdx.x, a.BH * a.Tm);
+  const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[pos]) : pos;
   const int bh = item / a.Tm, qb = item % a.Tm;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
@@ -426,7 +429,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = w % KW, qh = w / KW;
-  const int item = xcd_item(blockIdx.x, a.BH * a.Tn);
+  const int pos = xcd_item(blockIdx.x, a.BH * a.Tn);
+  const int item = a.col_order ? __builtin_amdgcn_readfirstlane(a.col_order[pos]) : pos;
   const int bh = item / a.Tn, kb = item % a.Tn;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
@@ -654,6 +658,7 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
   BwdArgs a{q, k, v, o, o_f32, lse, dout,
             m ? m->row_cnt : nullptr, m ? m->row_idx : nullptr,
             m ? m->col_cnt : nullptr, m ? m->col_idx : nullptr,
+            m ? m->row_order : nullptr, m ? m->col_order : nullptr,
             dq, dk, dv, dvec, s.N, s.Tm, s.Tn, s.BH(),
             (float)(1.4426950408889634 / sqrt((double)s.D)), (float)(1.0 / sqrt((double)s.D))};
   const int tpr = s.D * (s.dtype == SPA2_BF16 ? 2 : 4) / 16;

@@ -33,6 +33,7 @@ struct FwdArgs {
   float* o_f32;  // optional unrounded copy of O
   const int32_t* row_cnt;  // nullptr: dense
   const int32_t* row_idx;
+  const int32_t* row_order;  // optional scheduling order of the query blocks
   int N, Tm, Tn, items;
   float scale_log2;  // log2(e) / sqrt(D)
 };
@@ -57,7 +58,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int item = xcd_item(blockIdx.x, a.items);
+  const int pos = xcd_item(blockIdx.x, a.items);
+  const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[pos]) : pos;
   const int bh = item / a.Tm, qb = item % a.Tm;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
@@ -260,9 +262,10 @@ template <typename T, int BQ>
 constexpr int fwd_waves() { return 4; }
 
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
-                      const int32_t* row_cnt, const int32_t* row_idx, void* o, float* lse,
-                      float* o_f32, hipStream_t st) {
-  FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, s.N, s.Tm, s.Tn, s.BH() * s.Tm,
+                      const int32_t* row_cnt, const int32_t* row_idx, const int32_t* row_order,
+                      void* o, float* lse, float* o_f32, hipStream_t st) {
+  FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, row_cnt ? row_order : nullptr, s.N, s.Tm,
+            s.Tn, s.BH() * s.Tm,
             (float)(1.4426950408889634 / sqrt((double)s.D))};
   const dim3 grid(s.BH() * s.Tm);
 #define SPA2_FWD(T, D, BQ)                                               \

@@ -25,12 +25,13 @@ hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar,
 // from_scores: src holds raw pooled scores (softmax applied here); else src holds P-bar.
 hipError_t launch_select(const Shape& s, const double* src, bool from_scores, double* pbar_out,
                          int n_k, double p_frac, const spa2_blockmask& m, hipStream_t st);
+hipError_t launch_order(const int32_t* cnt, int items, int maxc, int32_t* order, hipStream_t st);
 hipError_t launch_rows(const Shape& s, const spa2_blockmask& m, hipStream_t st);
 hipError_t launch_cols(const Shape& s, const spa2_blockmask& m, hipStream_t st);
 
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
-                      const int32_t* row_cnt, const int32_t* row_idx, void* o, float* lse,
-                      float* o_f32, hipStream_t st);
+                      const int32_t* row_cnt, const int32_t* row_idx, const int32_t* row_order,
+                      void* o, float* lse, float* o_f32, hipStream_t st);
 // stage bits for launch_bwd
 constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7;
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,

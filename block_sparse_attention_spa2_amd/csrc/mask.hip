@@ -416,6 +416,57 @@ hipError_t launch_select(const Shape& s, const double* src, bool from_scores, do
   return hipGetLastError();
 }
 
+// Scheduling order: the item range [0, items) is cut into eight contiguous parts like
+// xcd_item() cuts it; workgroup x lists part x by count, largest first (a counting sort;
+// items of equal count land in the order of their atomic increments).
+__global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cnt, int items,
+                                                    int maxc, int32_t* __restrict__ order) {
+  __shared__ int hist[kMaxTn + 1];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, x = blockIdx.x;
+  const int q = items >> 3, r = items & 7;
+  const int lo = x * q + min(x, r), n = q + (x < r ? 1 : 0);
+  const int nb = maxc + 1;
+  for (int c = tid; c < nb; c += 256) hist[c] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 256) atomicAdd(&hist[min(max(cnt[lo + i], 0), maxc)], 1);
+  __syncthreads();
+  // start of count c = number of items with a larger count: thread t owns the bins
+  // u = maxc - c in [t per, (t + 1) per), counted from the top
+  const int per = (nb + 255) / 256;
+  int local = 0;
+  for (int k = 0; k < per; ++k) {
+    const int u = tid * per + k;
+    if (u < nb) local += hist[maxc - u];
+  }
+  int inc = local;  // inclusive scan over the threads
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if ((tid & 63) >= o) inc += y;
+  }
+  if ((tid & 63) == 63) wsum[tid >> 6] = inc;
+  __syncthreads();
+  int run = inc - local;
+  for (int wv = 0; wv < (tid >> 6); ++wv) run += wsum[wv];
+  for (int k = 0; k < per; ++k) {
+    const int u = tid * per + k;
+    if (u < nb) {
+      const int c = maxc - u, h = hist[c];
+      hist[c] = run;
+      run += h;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 256)
+    order[lo + atomicAdd(&hist[min(max(cnt[lo + i], 0), maxc)], 1)] = lo + i;
+}
+
+hipError_t launch_order(const int32_t* cnt, int items, int maxc, int32_t* order, hipStream_t st) {
+  order_kernel<<<8, 256, 0, st>>>(cnt, items, maxc, order);
+  return hipGetLastError();
+}
+
 hipError_t launch_rows(const Shape& s, const spa2_blockmask& m, hipStream_t st) {
   const int rows = s.BH() * s.Tm;
   rows_kernel<<<(rows + 255) / 256, 256, 0, st>>>(m.mask, rows, s.Tn, m.row_cnt, m.row_idx);

@@ -67,13 +67,22 @@ typedef struct {
  *   row_idx int32 [B, H, T_m, T_n]   their indices, ascending; entries past row_cnt unused
  *   col_cnt int32 [B, H, T_n]        query blocks that keep each key block
  *   col_idx int32 [B, H, T_n, T_m]   their indices, ascending; entries past col_cnt unused
- * The forward reads the row lists; the backward reads both. */
+ *   row_order int32 [B, H, T_m]      optional (NULL = natural order): the order in which
+ *                                    the attention kernels take query blocks
+ *   col_order int32 [B, H, T_n]      optional: the same for key blocks (dK/dV pass)
+ * The forward reads the row lists; the backward reads both. The orders only schedule work
+ * (results do not depend on them): the flattened block index range is cut into eight
+ * contiguous parts (one per XCD of the GPU, sharing an L2 cache) and each part lists its
+ * blocks by kept count, largest first, so that the longest rows start first; blocks of
+ * equal count appear in no particular order. The mask calls write them when non-NULL. */
 typedef struct {
   uint8_t* mask;
   int32_t* row_cnt;
   int32_t* row_idx;
   int32_t* col_cnt;
   int32_t* col_idx;
+  int32_t* row_order;
+  int32_t* col_order;
 } spa2_blockmask;
 
 /* Text for a status code (static storage). */

@@ -272,3 +272,39 @@ def test_o_f32_is_unrounded_o():
     o, _ = spa2.fwd(d["q"], d["k"], d["v"], _oracle_bm(r), o_f32=of)
     assert torch.equal(of.to(torch.bfloat16), o)
     gu.check_close("O f32", of.cpu().numpy().astype(np.float64), r["o"], "bf16")
+
+
+def _xcd_ranges(items):
+    q, r = items // 8, items % 8
+    lo = 0
+    for x in range(8):
+        n = q + (1 if x < r else 0)
+        yield lo, lo + n
+        lo += n
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "mid_bf16", "tiny_fp32"])
+def test_schedule_order(name):
+    """row_order / col_order: each of the eight contiguous index ranges is a permutation of
+    itself with kept counts non-increasing; outputs do not depend on the order."""
+    r = ref(name)
+    d = r["dev"]
+    bm = spa2.mask(d["q"], d["k"], r["k"], r["p"], r["bq"], r["bkv"])
+    for cnt_t, ord_t in ((bm.row_cnt, bm.row_order), (bm.col_cnt, bm.col_order)):
+        cnt = cnt_t.cpu().numpy().reshape(-1)
+        order = ord_t.cpu().numpy().reshape(-1)
+        for lo, hi in _xcd_ranges(cnt.size):
+            part = order[lo:hi]
+            assert np.array_equal(np.sort(part), np.arange(lo, hi))
+            assert np.all(np.diff(cnt[part]) <= 0)
+    natural = spa2.BlockMask(bm.mask, bm.row_cnt, bm.row_idx, bm.col_cnt, bm.col_idx,
+                             bm.bq, bm.bkv)
+    of1 = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    of2 = torch.empty_like(of1)
+    o1, l1 = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of1)
+    o2, l2 = spa2.fwd(d["q"], d["k"], d["v"], natural, o_f32=of2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(of1, of2)
+    g1 = spa2.bwd(d["q"], d["k"], d["v"], o1, l1, d["do"], bm, o_f32=of1)
+    g2 = spa2.bwd(d["q"], d["k"], d["v"], o2, l2, d["do"], natural, o_f32=of2)
+    for a_, b_ in zip(g1, g2):
+        assert torch.equal(a_, b_)
