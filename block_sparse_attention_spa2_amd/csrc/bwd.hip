@@ -91,10 +91,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 //    block j) is removed at the end.
 // c_j = the block's first key row; what remains involves only K_k - c_j. Both terms are
 // rank-one updates per block, w_j (x) c_j with w_j = sum_k r_k or P^blk_j. They are
-// batched on the matrix unit: the c_j of 32 consecutive blocks are copied into an LDS
-// matrix C (32 x D) and the weights into an MFMA operand W (32 x 16 queries per tile), and
-// every 32 blocks acc += C^T W, pkc += C^T W'. sum_k bf16(dS_k) comes from the matrix unit
-// too (a ones operand times the packed dS), so sum_k r_k costs one add per element.
+// batched on the matrix unit, eight blocks at a time: each lane group g (16 lanes, a
+// quarter of the block's keys) keeps its partial weights of the last eight blocks as the
+// eight reduction slots 8g .. 8g + 7 of an MFMA operand W, and an LDS matrix C holds c_j
+// of those blocks so that slot 8g + i of the other operand is c_i for every g. One MFMA
+// per output tile then sums the partials over the groups and the blocks: acc += C^T W,
+// pkc += C^T W'. The groups' partials of sum_k bf16(dS_k) come from the matrix unit too
+// (a 0/1 operand times the packed dS), so sum_k r_k costs one add per element.
 // ------------------------------------------------------------------------------------
 template <typename T, int D, int BQ, bool DENSE, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
@@ -168,24 +171,26 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 
   f32x4 acc[DT][QT], pkc[DT][QT];
   float tpart[QT];
-  // correction weights: wr / wp hold the last eight blocks' sum_k r_k / P^blk (bf16, the
-  // newest in element 7); every four blocks the newest four move into the batch operands
-  // Wr / Wp at the slots of their C rows.
-  u32x4 wr[QT], wp[QT], Wr[QT], Wp[QT];
+  // correction weights: wr / wp hold this lane group's partial sum_k r_k / P^blk of the
+  // last eight blocks (bf16, the newest in element 7): at the end of a batch of eight,
+  // element i is block i of the batch.
+  u32x4 wr[QT], wp[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     tpart[qt] = 0.f;
-    wr[qt] = wp[qt] = Wr[qt] = Wp[qt] = u32x4{0u, 0u, 0u, 0u};
+    wr[qt] = wp[qt] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       acc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
       pkc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  // ones in row 0 of a 16 x 32 A operand: C row 0 = the column sums of B
+  // A operand with ones where the reduction slot belongs to lane group m % 4 (row m): row
+  // m of C sums the column over the slots of lane group m % 4 only, so element g of lane
+  // group g receives the sum over its own 16 keys
   F ones = E::zero();
   if constexpr (kCorr) {
-    if (c16 == 0)
+    if (g == (c16 & 3))
 #pragma unroll
       for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
   }
@@ -195,38 +200,21 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     r = u32x4{__builtin_amdgcn_alignbit(r[1], r[0], 16), __builtin_amdgcn_alignbit(r[2], r[1], 16),
               __builtin_amdgcn_alignbit(r[3], r[2], 16), __builtin_amdgcn_alignbit(b, r[3], 16)};
   };
-  // the four newest blocks are batch rows 4 qd .. 4 qd + 3, qd = (t % 32) / 4: A slots
-  // 0..3 of lane group qd (qd < 4) or slots 4..7 of group qd - 4 (qd >= 4)
-  auto commit = [&](int t) {
-    const int qd = (t & 31) >> 2;
-    if (g == (qd & 3)) {
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        if (qd < 4) {
-          Wr[qt][0] = wr[qt][2]; Wr[qt][1] = wr[qt][3];
-          Wp[qt][0] = wp[qt][2]; Wp[qt][1] = wp[qt][3];
-        } else {
-          Wr[qt][2] = wr[qt][2]; Wr[qt][3] = wr[qt][3];
-          Wp[qt][2] = wp[qt][2]; Wp[qt][3] = wp[qt][3];
-        }
-      }
-    }
-  };
+  // C rows: block i of a batch at rows 4 g' + i (i < 4) or 16 + 4 g' + (i - 4), g' = 0..3,
+  // so that the transpose reads of every lane group see c_0 .. c_7 in slots 0..7
   auto flush = [&](const char* cmb) {
     if constexpr (kCorr) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      F ca;
-      CM::read_col4(cmb, 0, dt * 16, ca, 0);
-      CM::read_col4(cmb, 16, dt * 16, ca, 1);
+      for (int dt = 0; dt < DT; ++dt) {
+        F ca;
+        CM::read_col4(cmb, 0, dt * 16, ca, 0);
+        CM::read_col4(cmb, 16, dt * 16, ca, 1);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        acc[dt][qt] = E::mma(ca, __builtin_bit_cast(F, Wr[qt]), acc[dt][qt]);
-        pkc[dt][qt] = E::mma(ca, __builtin_bit_cast(F, Wp[qt]), pkc[dt][qt]);
+        for (int qt = 0; qt < QT; ++qt) {
+          acc[dt][qt] = E::mma(ca, __builtin_bit_cast(F, wr[qt]), acc[dt][qt]);
+          pkc[dt][qt] = E::mma(ca, __builtin_bit_cast(F, wp[qt]), pkc[dt][qt]);
+        }
       }
-    }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) Wr[qt] = Wp[qt] = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -247,12 +235,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     const char* Kb = stage;
     const char* Vb = stage + KV::kBytes;
     if constexpr (kCorr) {
-      // the previous batch's C rows are now visible to every wave
-      if ((t & 31) == 0 && t > 0) flush(((t >> 5) & 1) ? cm0 : cm1);
-      // row t % 32 of this batch's C: the block's first key row
-      if (w == 0 && l < 16) {
-        char* cmw = ((t >> 5) & 1) ? cm1 : cm0;
-        CM::store_chunk(cmw, t & 31, l, *reinterpret_cast<const u32x4*>(Kb + KV::offset(0, l * 8)));
+      // the previous batch's C rows are now visible to every wave; its weights are the
+      // shift registers' contents (this block has not shifted in yet)
+      if ((t & 7) == 0 && t > 0) flush(((t >> 3) & 1) ? cm0 : cm1);
+      // this block's first key row, four copies (one per lane group)
+      if (w == 0) {
+        const int i = t & 7, c = l & 15, gg = l >> 4;
+        const int row = (i < 4 ? i : 12 + i) + 4 * gg;
+        char* cmw = ((t >> 3) & 1) ? cm1 : cm0;
+        CM::store_chunk(cmw, row, c, *reinterpret_cast<const u32x4*>(Kb + KV::offset(0, c * 8)));
       }
     }
 
@@ -305,7 +296,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
           }
         }
 
-    f32x4 cs[QT];  // row 0: sum_k bf16(dS_k) of this block, per query column
+    f32x4 cs[QT];  // element g: sum of bf16(dS_k) over this lane group's keys
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) cs[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -329,12 +320,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         tpart[qt] += tb[qt];
-        // cs row 0 lives in lanes of group 0, element 0; the other groups hold zeros
-        const float bsum = sum4(g == 0 ? cs[qt][0] : 0.f);
-        shift_in(wr[qt], sum4(tb[qt]) - bsum);
-        shift_in(wp[qt], sum4(pb[qt]));
+        // this group's share of sum_k r_k: its fp32 partial of sum_k dS_k minus its partial
+        // of sum_k bf16(dS_k) (small: bf16 keeps the weight's own rounding negligible)
+        const float bsum = g == 0 ? cs[qt][0] : g == 1 ? cs[qt][1] : g == 2 ? cs[qt][2] : cs[qt][3];
+        shift_in(wr[qt], tb[qt] - bsum);
+        shift_in(wp[qt], pb[qt]);
       }
-      if ((t & 3) == 3) commit(t);
     }
   };
   if constexpr (NS == 3) {
@@ -352,19 +343,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 
   if constexpr (kCorr) {
     if (cnt > 0) {
-      // complete the last quad with zero weights, then apply the last batch
+      // complete the last batch with zero weights, then apply it
       const int last = cnt - 1;
-      if ((last & 3) != 3) {
-        for (int t = last + 1; (t & 3) != 0; ++t)
+      for (int t = last + 1; (t & 7) != 0; ++t)
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            shift_in(wr[qt], 0.f);
-            shift_in(wp[qt], 0.f);
-          }
-        commit(last | 3);
-      }
-      __syncthreads();  // the last C row written is visible
-      flush(((last >> 5) & 1) ? cm1 : cm0);
+        for (int qt = 0; qt < QT; ++qt) {
+          shift_in(wr[qt], 0.f);
+          shift_in(wp[qt], 0.f);
+        }
+      __syncthreads();  // the last C rows written are visible
+      flush(((last >> 3) & 1) ? cm1 : cm0);
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
