@@ -110,10 +110,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   using KV = Tile<T, BKV, D>;
   constexpr bool kCorr = sizeof(T) == 2;
   using CM = Tile<T, 32, D>;  // c_j of one batch of 32 blocks (bf16 only)
-  // K/V stages in separate LDS variables, named statically (see the forward kernel): three
-  // (loads issued two blocks ahead) when they fit next to C, else two
+  // K/V stages in separate LDS variables, named statically (see the forward kernel). The
+  // code also runs three stages (loads issued two blocks ahead, partial vmcnt waits), which
+  // measured slower than two with eight waves per workgroup.
   constexpr int kStageBytes = 2 * KV::kBytes;
-  constexpr int NS = kCorr && 3 * kStageBytes + 2 * CM::kBytes <= 160 * 1024 ? 3 : 2;
+  constexpr int NS = 2;
   __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char stage1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char stage2[NS == 3 ? kStageBytes : 16];
