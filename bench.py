@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "fwd": ("fwd.hip", "common.h", "kernels.h"),
     "bwd_dkdv": ("bwd.hip", "common.h", "kernels.h"),
-    "bwd_dq": ("bwd.hip", "common.h", "kernels.h"),
+    "bwd_dq_rowterm": ("bwd.hip", "common.h", "kernels.h"),
 }
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_wan13b_480p.txt")
 
@@ -190,18 +190,15 @@ def main():
     def stage_fwd():
         spa2.fwd(q, k, v, bm, out=(o, lse), o_f32=o_f32)
 
-    def stage_prep():
-        spa2.bwd_prep(o, do, dvec, bq, bkv, o_f32=o_f32)
+    def stage_dq():  # dQ and the row term rowsum(dO * O), which the dK/dV pass reads
+        spa2.bwd_dq_rowterm(q, k, v, o, lse, do, dvec, bm, dq, o_f32=o_f32)
 
     def stage_dkdv():
         spa2.bwd_dkdv(q, k, v, lse, do, dvec, bm, dk, dv)
 
-    def stage_dq():
-        spa2.bwd_dq(q, k, v, lse, do, dvec, bm, dq)
-
     stages = [("mask", stage_mask), ("fwd", stage_fwd)]
     if train:
-        stages += [("bwd_prep", stage_prep), ("bwd_dkdv", stage_dkdv), ("bwd_dq", stage_dq)]
+        stages += [("bwd_dq_rowterm", stage_dq), ("bwd_dkdv", stage_dkdv)]
 
     for _ in range(args.warmup):
         for _, fn in stages:
@@ -280,7 +277,7 @@ def main():
 
     kernel_flops = {"fwd": flops_fwd}
     if train:
-        kernel_flops.update(bwd_dkdv=8.0 * D * area, bwd_dq=2.0 * D * area)
+        kernel_flops.update(bwd_dkdv=8.0 * D * area, bwd_dq_rowterm=2.0 * D * area)
     dom = max(kernel_flops, key=lambda n: per_stage[n])
     achieved = kernel_flops[dom] / (per_stage[dom] * 1e-3) / 1e12
     roofline = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2),

@@ -287,3 +287,23 @@ def bwd_dq(q, k, v, lse, do, dvec, bm: BlockMask | None, dq, bq: int = 128, bkv:
         C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dvec),
         bmc, _ptr(dq), _stream(q)))
     return dq
+
+
+def bwd_dq_rowterm(q, k, v, o, lse, do, dvec, bm: BlockMask | None, dq, bq: int = 128,
+                   bkv: int = 64, *, o_f32: torch.Tensor | None = None):
+    """dQ pass that also writes the row term dvec = rowsum(dO * O) (O = o_f32 if given);
+    bwd runs it before the dK/dV pass, which reads dvec."""
+    if bm is not None:
+        bq, bkv = bm.bq, bm.bkv
+        _check_bm(bm, q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq)):
+        _expect(name, t, q.shape, q.dtype)
+    if o_f32 is not None:
+        _expect("o_f32", o_f32, q.shape, torch.float32)
+    _expect("lse", lse, q.shape[:3], torch.float32)
+    _expect("dvec", dvec, q.shape[:3], torch.float32)
+    bmc = C.byref(bm.c()) if bm is not None else None
+    _lib.check("spa2_bwd_dq_rowterm", _lib.lib().spa2_bwd_dq_rowterm(
+        C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_f32), _ptr(lse),
+        _ptr(do), bmc, _ptr(dvec), _ptr(dq), _stream(q)))
+    return dq

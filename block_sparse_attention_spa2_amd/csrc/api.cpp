@@ -205,8 +205,22 @@ spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const 
   if (m && (!m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
   if (!workspace || ws_bytes < (size_t)s.BH() * s.N * sizeof(float)) return SPA2_E_WORKSPACE;
   return hip_status("bwd", spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, dk, dv,
-                                            (float*)workspace, spa2::kBwdAll,
+                                            (float*)workspace, spa2::kBwdDqRow | spa2::kBwdDkdv,
                                             (hipStream_t)stream));
+}
+
+spa2_status spa2_bwd_dq_rowterm(const spa2_desc* desc, const void* q, const void* k,
+                                const void* v, const void* o, const float* o_f32,
+                                const float* lse, const void* dout,
+                                const spa2_blockmask* m, float* dvec, void* dq, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dvec || !dq) return SPA2_E_NULL;
+  if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
+  return hip_status("bwd_dq_rowterm",
+                    spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, nullptr, nullptr,
+                                     dvec, spa2::kBwdDqRow, (hipStream_t)stream));
 }
 
 spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f32,

@@ -41,6 +41,7 @@ struct BwdArgs {
   void* dv;
   float* dvec;
   int N, Tm, Tn, BH;
+  int rowterm;  // dQ pass: compute Dv = rowsum(dO * O) itself and store it in dvec
   float scale_log2;  // log2(e) / sqrt(D)
   float scale;       // 1 / sqrt(D)
 };
@@ -167,7 +168,34 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
       df[qt][ks] = ok ? load_row8<T>(dO + (size_t)row * D + ks * 32 + 8 * g) : E::zero();
     }
     lse2[qt] = ok ? a.lse[(size_t)bh * N + row] * kLog2e : INFINITY;
-    dv[qt] = ok ? a.dvec[(size_t)bh * N + row] : 0.f;
+    if (a.rowterm) {
+      // Dv = rowsum(dO * O) from the dO fragments already held (lane: 8 columns per ks)
+      // and the same columns of O (o_f32 when given), summed over the 4 lanes of the row
+      float part = 0.f;
+      if (ok) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const size_t off = (size_t)row * D + ks * 32 + 8 * g;
+          if (a.o_f32) {
+            const f32x4 o0 = *reinterpret_cast<const f32x4*>(a.o_f32 + head + off);
+            const f32x4 o1 = *reinterpret_cast<const f32x4*>(a.o_f32 + head + off + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              part += E::to_f32(df[qt][ks][e]) * o0[e];
+              part += E::to_f32(df[qt][ks][4 + e]) * o1[e];
+            }
+          } else {
+            const F of = load_row8<T>((const T*)a.o + head + off);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += E::to_f32(df[qt][ks][e]) * E::to_f32(of[e]);
+          }
+        }
+      }
+      dv[qt] = sum4(part);
+      if (ok && g == 0) a.dvec[(size_t)bh * N + row] = dv[qt];
+    } else {
+      dv[qt] = ok ? a.dvec[(size_t)bh * N + row] : 0.f;
+    }
   }
 
   f32x4 acc[DT][QT], pkc[DT][QT];
@@ -648,7 +676,7 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
             m ? m->row_cnt : nullptr, m ? m->row_idx : nullptr,
             m ? m->col_cnt : nullptr, m ? m->col_idx : nullptr,
             m ? m->row_order : nullptr, m ? m->col_order : nullptr,
-            dq, dk, dv, dvec, s.N, s.Tm, s.Tn, s.BH(),
+            dq, dk, dv, dvec, s.N, s.Tm, s.Tn, s.BH(), 0,
             (float)(1.4426950408889634 / sqrt((double)s.D)), (float)(1.0 / sqrt((double)s.D))};
   const int tpr = s.D * (s.dtype == SPA2_BF16 ? 2 : 4) / 16;
   const int rpb = 256 / tpr;
@@ -657,14 +685,20 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
   const dim3 gq(s.BH() * s.Tm), gk(s.BH() * s.Tn);
 #define SPA2_BWD(T, D, BQ)                                                       \
   do {                                                                           \
+    constexpr int nq = sizeof(T) == 2 ? BQ / 16 : 4;                            \
     if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);        \
+    if (stages & kBwdDqRow) { /* dQ and the row term first: dK/dV reads dvec */  \
+      a.rowterm = 1;                                                             \
+      if (m) bwd_dq_kernel<T, D, BQ, false, nq><<<gq, 64 * nq, 0, st>>>(a);     \
+      else bwd_dq_kernel<T, D, BQ, true, nq><<<gq, 64 * nq, 0, st>>>(a);        \
+      a.rowterm = 0;                                                             \
+    }                                                                            \
     if (stages & kBwdDkdv) {                                                     \
       constexpr int nw = sizeof(T) == 2 ? 8 : 4, kt = dkdv_key_tiles<T, BQ>(); \
       if (m) bwd_dkdv_kernel<T, D, BQ, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
       else bwd_dkdv_kernel<T, D, BQ, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a);    \
     }                                                                            \
     if (stages & kBwdDq) {                                                       \
-      constexpr int nq = sizeof(T) == 2 ? BQ / 16 : 4;                          \
       if (m) bwd_dq_kernel<T, D, BQ, false, nq><<<gq, 64 * nq, 0, st>>>(a);     \
       else bwd_dq_kernel<T, D, BQ, true, nq><<<gq, 64 * nq, 0, st>>>(a);        \
     }                                                                            \

@@ -33,7 +33,9 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
                       const int32_t* row_cnt, const int32_t* row_idx, const int32_t* row_order,
                       void* o, float* lse, float* o_f32, hipStream_t st);
 // stage bits for launch_bwd
-constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdAll = 7;
+// kBwdDqRow: the dQ pass that also computes the row term (instead of kBwdPrep), run
+// before the dK/dV pass.
+constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdDqRow = 8, kBwdAll = 7;
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* o_f32, const float* lse, const void* dout, const spa2_blockmask* m, void* dq,
                       void* dk, void* dv, float* dvec, int stages, hipStream_t st);

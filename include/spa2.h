@@ -153,13 +153,21 @@ spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const 
                      const spa2_blockmask* m, void* dq, void* dk, void* dv, void* workspace,
                      size_t ws_bytes, void* stream);
 
-/* The three kernels of spa2_bwd, callable one by one (for example to run the dK/dV pass
- * and the dQ pass on two streams once the preprocess has finished). spa2_bwd is exactly
- * spa2_bwd_prep, then spa2_bwd_dkdv, then spa2_bwd_dq on one stream.
- *   spa2_bwd_prep: dvec[B, H, N] (float, device) = rowsum(dO * O), O = o_f32 if given;
+/* The passes of spa2_bwd, callable one by one (for example to time them, or to run the
+ * dK/dV pass on another stream). spa2_bwd is exactly spa2_bwd_dq_rowterm, then
+ * spa2_bwd_dkdv, on one stream.
+ *   spa2_bwd_dq_rowterm: dQ from the row lists (one workgroup per query block), and the
+ *                  row term dvec[B, H, N] (float, device) = rowsum(dO * O), O = o_f32 if
+ *                  given, computed by the same pass from the dO rows it loads anyway;
  *   spa2_bwd_dkdv: dK, dV from the column lists (one workgroup per key block);
- *   spa2_bwd_dq:   dQ from the row lists (one workgroup per query block).
- * dvec must hold spa2_bwd_prep's result for the same O and dO. */
+ *   spa2_bwd_prep: the row term alone (a separate pass over O and dO);
+ *   spa2_bwd_dq:   dQ alone, reading dvec.
+ * dvec must hold the row term for the same O and dO (from either pass; the two sum in
+ * different orders, so results agree to rounding, not bit for bit). */
+spa2_status spa2_bwd_dq_rowterm(const spa2_desc* desc, const void* q, const void* k,
+                                const void* v, const void* o, const float* o_f32,
+                                const float* lse, const void* dout,
+                                const spa2_blockmask* m, float* dvec, void* dq, void* stream);
 spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f32,
                           const void* dout, float* dvec, void* stream);
 spa2_status spa2_bwd_dkdv(const spa2_desc* desc, const void* q, const void* k, const void* v,

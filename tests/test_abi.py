@@ -75,6 +75,8 @@ def test_bad_desc(kw, code):
     assert L.spa2_bwd_prep(C.byref(d), FAKE, None, FAKE, FAKE, None) == code
     assert L.spa2_bwd_dkdv(C.byref(d), *[FAKE] * 6, None, FAKE, FAKE, None) == code
     assert L.spa2_bwd_dq(C.byref(d), *[FAKE] * 6, None, FAKE, None) == code
+    assert L.spa2_bwd_dq_rowterm(C.byref(d), *[FAKE] * 4, None, FAKE, FAKE, None, FAKE, FAKE,
+                                 None) == code
     n = C.c_size_t(0)
     assert L.spa2_mask_workspace_size(C.byref(d), C.byref(n)) == code
 
@@ -122,6 +124,14 @@ def test_null_pointers():
     assert L.spa2_bwd_dkdv(d, *st, C.byref(bm(col_idx=None)), FAKE, FAKE, None) == _lib.E_NULL
     assert L.spa2_bwd_dq(d, *st, C.byref(bm(row_cnt=None)), FAKE, None) == _lib.E_NULL
     assert L.spa2_bwd_dq(d, *st, None, None, None) == _lib.E_NULL
+    # dQ with the row term: q k v o o_f32 lse dout m dvec dq stream
+    rargs = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 2 + [None]
+    for i in (0, 1, 2, 3, 5, 6, 8, 9):
+        a = list(rargs)
+        a[i] = None
+        assert L.spa2_bwd_dq_rowterm(d, *a) == _lib.E_NULL, i
+    assert L.spa2_bwd_dq_rowterm(d, *rargs[:7], C.byref(bm(row_idx=None)),
+                                 *rargs[8:]) == _lib.E_NULL
     assert L.spa2_pool(d, FAKE, None, FAKE, FAKE, None) == _lib.E_NULL
     assert L.spa2_mask_lists(d, C.byref(bm(mask=None)), None) == _lib.E_NULL
 

@@ -264,6 +264,36 @@ def test_bwd_without_unrounded_o(name):
         gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
 
 
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_f32_d64_bq128",
+                                  "single_block"])
+def test_staged_backward(name):
+    """The staged entry points against the oracle: dQ with the row term then dK/dV (bit for
+    bit what spa2_bwd does), and the three-pass form with the separate row-term pass."""
+    r = ref(name)
+    d = r["dev"]
+    bm = _oracle_bm(r)
+    of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
+    g1 = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
+    dvec = torch.empty_like(lse)
+    dq = spa2.bwd_dq_rowterm(d["q"], d["k"], d["v"], o, lse, d["do"], dvec, bm,
+                             torch.empty_like(o), o_f32=of)
+    dk, dv = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec, bm,
+                           torch.empty_like(o), torch.empty_like(o))
+    for a, b in zip(g1, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    # row term against its definition, rowsum(dO * O) in float64
+    want = (d["do"].double() * of.double()).sum(-1)
+    assert torch.allclose(dvec.double(), want, rtol=1e-5, atol=1e-6 * want.abs().max().item())
+    dvec3 = torch.empty_like(lse)
+    spa2.bwd_prep(o, d["do"], dvec3, o_f32=of)
+    dk3, dv3 = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm,
+                             torch.empty_like(o), torch.empty_like(o))
+    dq3 = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm, torch.empty_like(o))
+    for nm, got, want in (("dQ", dq3, r["dq"]), ("dK", dk3, r["dk"]), ("dV", dv3, r["dv"])):
+        gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
+
+
 def test_o_f32_is_unrounded_o():
     """o_f32 rounds (to nearest even) to exactly the O written in the input dtype."""
     r = ref("ragged_bf16")
