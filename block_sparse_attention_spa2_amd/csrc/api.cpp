@@ -65,14 +65,18 @@ spa2_status hip_status(const char* where, hipError_t e) {
   return SPA2_E_HIP;
 }
 
-// Lists are complete: write the scheduling orders the caller asked for.
+// Lists are complete: write the scheduling orders the caller asked for. Query blocks go
+// head by head within each XCD's part (the forward and dQ passes then share K/V tiles in
+// L2); key blocks go longest first across the whole part (a head's attention-sink column
+// can hold most of the query blocks and must start first).
 spa2_status write_orders(const spa2::Shape& s, const spa2_blockmask& m, hipStream_t hs) {
   spa2_status st = SPA2_OK;
   if (m.row_order &&
-      (st = hip_status("order", spa2::launch_order(m.row_cnt, s.BH() * s.Tm, s.Tn, m.row_order, hs))) != SPA2_OK)
+      (st = hip_status("order", spa2::launch_order(m.row_cnt, s.BH() * s.Tm, s.Tn, s.Tm,
+                                                   m.row_order, hs))) != SPA2_OK)
     return st;
   if (m.col_order)
-    st = hip_status("order", spa2::launch_order(m.col_cnt, s.BH() * s.Tn, s.Tm, m.col_order, hs));
+    st = hip_status("order", spa2::launch_order(m.col_cnt, s.BH() * s.Tn, s.Tm, 0, m.col_order, hs));
   return st;
 }
 

@@ -25,7 +25,8 @@ hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar,
 // from_scores: src holds raw pooled scores (softmax applied here); else src holds P-bar.
 hipError_t launch_select(const Shape& s, const double* src, bool from_scores, double* pbar_out,
                          int n_k, double p_frac, const spa2_blockmask& m, hipStream_t st);
-hipError_t launch_order(const int32_t* cnt, int items, int maxc, int32_t* order, hipStream_t st);
+hipError_t launch_order(const int32_t* cnt, int items, int maxc, int per_head, int32_t* order,
+                        hipStream_t st);
 hipError_t launch_rows(const Shape& s, const spa2_blockmask& m, hipStream_t st);
 hipError_t launch_cols(const Shape& s, const spa2_blockmask& m, hipStream_t st);
 

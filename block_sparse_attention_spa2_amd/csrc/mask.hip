@@ -417,27 +417,42 @@ hipError_t launch_select(const Shape& s, const double* src, bool from_scores, do
 }
 
 // Scheduling order: the item range [0, items) is cut into eight contiguous parts like
-// xcd_item() cuts it; workgroup x lists part x by count, largest first (a counting sort;
-// items of equal count land in the order of their atomic increments).
+// xcd_item() cuts it; workgroup x lists part x by a counting sort. With per_head = 0 the
+// key is the kept count, largest first. With per_head > 0 (items per head) the part is
+// listed head by head, each head's items largest first, so the workgroups that run at the
+// same time on one XCD mostly read one head's tiles (more L2 reuse); if the part spans too
+// many heads for the histogram, the plain order is used. Items with equal keys land in the
+// order of their atomic increments.
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cnt, int items,
-                                                    int maxc, int32_t* __restrict__ order) {
-  __shared__ int hist[kMaxTn + 1];
+                                                    int maxc, int per_head,
+                                                    int32_t* __restrict__ order) {
+  constexpr int kBins = 16384;
+  static_assert(kBins >= kMaxTn + 1, "the plain order always fits");
+  __shared__ int hist[kBins];
   __shared__ int wsum[4];
   const int tid = threadIdx.x, x = blockIdx.x;
   const int q = items >> 3, r = items & 7;
   const int lo = x * q + min(x, r), n = q + (x < r ? 1 : 0);
   const int nb = maxc + 1;
-  for (int c = tid; c < nb; c += 256) hist[c] = 0;
+  const int h0 = per_head > 0 ? lo / per_head : 0;
+  const int nh = per_head > 0 && n > 0 ? (lo + n - 1) / per_head - h0 + 1 : 1;
+  const bool by_head = nh * nb <= kBins;
+  const int nbins = by_head ? nh * nb : nb;
+  // bin of item lo + i: (head within the part, then count from the top)
+  auto bin = [&](int i) {
+    const int c = min(max(cnt[lo + i], 0), maxc);
+    return (by_head && per_head > 0 ? ((lo + i) / per_head - h0) * nb : 0) + (maxc - c);
+  };
+  for (int c = tid; c < nbins; c += 256) hist[c] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += 256) atomicAdd(&hist[min(max(cnt[lo + i], 0), maxc)], 1);
+  for (int i = tid; i < n; i += 256) atomicAdd(&hist[bin(i)], 1);
   __syncthreads();
-  // start of count c = number of items with a larger count: thread t owns the bins
-  // u = maxc - c in [t per, (t + 1) per), counted from the top
-  const int per = (nb + 255) / 256;
+  // exclusive scan of the bins: thread t owns bins [t per, (t + 1) per)
+  const int per = (nbins + 255) / 256;
   int local = 0;
   for (int k = 0; k < per; ++k) {
     const int u = tid * per + k;
-    if (u < nb) local += hist[maxc - u];
+    if (u < nbins) local += hist[u];
   }
   int inc = local;  // inclusive scan over the threads
 #pragma unroll
@@ -451,19 +466,19 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
   for (int wv = 0; wv < (tid >> 6); ++wv) run += wsum[wv];
   for (int k = 0; k < per; ++k) {
     const int u = tid * per + k;
-    if (u < nb) {
-      const int c = maxc - u, h = hist[c];
-      hist[c] = run;
+    if (u < nbins) {
+      const int h = hist[u];
+      hist[u] = run;
       run += h;
     }
   }
   __syncthreads();
-  for (int i = tid; i < n; i += 256)
-    order[lo + atomicAdd(&hist[min(max(cnt[lo + i], 0), maxc)], 1)] = lo + i;
+  for (int i = tid; i < n; i += 256) order[lo + atomicAdd(&hist[bin(i)], 1)] = lo + i;
 }
 
-hipError_t launch_order(const int32_t* cnt, int items, int maxc, int32_t* order, hipStream_t st) {
-  order_kernel<<<8, 256, 0, st>>>(cnt, items, maxc, order);
+hipError_t launch_order(const int32_t* cnt, int items, int maxc, int per_head, int32_t* order,
+                        hipStream_t st) {
+  order_kernel<<<8, 256, 0, st>>>(cnt, items, maxc, per_head, order);
   return hipGetLastError();
 }
 
