@@ -287,6 +287,18 @@ def main():
                     flops_per_launch=kernel_flops[dom], ms_per_launch=round(per_stage[dom], 4))
     mask_bytes = 2.0 * B * H * N * D * q.element_size()  # Q and K read once
     copy_gbs = copy_bandwidth()
+    # every timed kernel against both ceilings: MFMA (algorithmic flops) and memory (the
+    # recorded counter bytes, when the kernel is unchanged since they were taken)
+    kernels = {}
+    for name, fl in kernel_flops.items():
+        t = per_stage[name] * 1e-3
+        rec = recorded_traffic(name, args.workload)
+        kernels[name] = {"ms": round(per_stage[name], 4), "tflops": round(fl / t / 1e12, 2),
+                         "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic_bytes": rec,
+                         "GB/s": None if rec is None else round(rec / t / 1e9, 1),
+                         "hbm_frac": None if rec is None else round(rec / t / 1e9 / PEAK_HBM_GBS, 4),
+                         "copy_frac": None if rec is None else round(rec / t / 1e9 / copy_gbs, 4)}
 
     cpu = None
     if not args.no_cpu:
@@ -321,6 +333,7 @@ def main():
                    "kept_area_tokens2": area,
                    "step": "mask+fwd+bwd" if train else "mask+fwd"},
         "roofline": roofline,
+        "kernels": kernels,
         "cpu_baseline": cpu,
         "stages_ms": {k_: round(v_, 4) for k_, v_ in per_stage.items()},
         "stages_spread_ms": spread,
@@ -368,7 +381,6 @@ def run_sweep(args):
         o, lse = torch.empty_like(q), torch.empty_like(ld)
         bm = spa2.BlockMask.empty(B, H, N, bq, bkv, q.device)
         mws = torch.empty(spa2.mask_workspace_size(q, bq, bkv), dtype=torch.uint8, device="cuda")
-        l1_dense = od32.abs().sum().item()
         grid = ([(kf, 0.0) for kf in configs.SWEEP_K] + [(0.0, pf) for pf in configs.SWEEP_P]
                 + [(kf, pf) for kf in configs.SWEEP_K for pf in configs.SWEEP_P])
         for kf, pf in grid:
@@ -384,15 +396,18 @@ def run_sweep(args):
                 torch.cuda.synchronize()
                 ts["mask"].append(e[0].elapsed_time(e[1]))
                 ts["fwd"].append(e[1].elapsed_time(e[2]))
-            tau = torch.exp(lse - ld).unsqueeze(-1)  # kept probability mass per row
-            e_drop = (od32 - tau * os32).abs().sum().item() / l1_dense
-            e_renorm = ((tau - 1.0) * os32).abs().sum().item() / l1_dense
+            # error decomposition (spa2_error_terms): sums of |O_dense|, |O_dense - O_sparse|,
+            # |dropped-mass term|, |renormalisation term| per head; tau per row
+            terms, tau = spa2.error_terms(os32, lse, od32, ld, bq, bkv, with_tau=True)
+            tot = terms.sum(dim=(0, 1)).tolist()
+            l1_dense = tot[0]
+            e_drop, e_renorm = tot[2] / l1_dense, tot[3] / l1_dense
             results.append({
                 "generator": wl, "mode": mode, "k": kf, "p": pf,
                 "kept_fraction": round(bm.mask.float().mean().item(), 6),
                 "mask_ms": round(_pct(ts["mask"][args.warmup:], 50), 4),
                 "fwd_ms": round(_pct(ts["fwd"][args.warmup:], 50), 4),
-                "rel_l1": round((os32 - od32).abs().sum().item() / l1_dense, 5),
+                "rel_l1": round(tot[1] / l1_dense, 5),
                 "rel_l1_dropped_mass": round(e_drop, 5),
                 "rel_l1_renormalisation": round(e_renorm, 5),
                 "mean_dropped_mass": round(float((1.0 - tau).mean().item()), 5),

@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import Spa2Error  # noqa: F401
 
 __all__ = ["BlockMask", "pool", "mask", "select", "mask_lists", "fwd", "bwd", "bwd_prep",
-           "bwd_dkdv", "bwd_dq",
+           "bwd_dkdv", "bwd_dq", "bwd_dq_rowterm", "error_terms",
            "mask_workspace_size", "bwd_workspace_size", "num_blocks", "Spa2Error"]
 
 
@@ -307,3 +307,22 @@ def bwd_dq_rowterm(q, k, v, o, lse, do, dvec, bm: BlockMask | None, dq, bq: int 
         C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_f32), _ptr(lse),
         _ptr(do), bmc, _ptr(dvec), _ptr(dq), _stream(q)))
     return dq
+
+
+def error_terms(o_sparse: torch.Tensor, lse_sparse: torch.Tensor, o_dense: torch.Tensor,
+                lse_dense: torch.Tensor, bq: int = 128, bkv: int = 64, *, with_tau: bool = False):
+    """Error decomposition of a sparse forward against the dense one, per head: float64
+    [B, H, 4] = sums of |O_dense|, |O_dense - O_sparse|, |dropped-mass term|,
+    |renormalisation term|; O in float32 (the o_f32 outputs of fwd). With with_tau, also
+    the per-row kept dense mass tau [B, H, N] (float32)."""
+    B, H = o_sparse.shape[:2]
+    for name, t in (("o_sparse", o_sparse), ("o_dense", o_dense)):
+        _expect(name, t, o_sparse.shape, torch.float32)
+    for name, t in (("lse_sparse", lse_sparse), ("lse_dense", lse_dense)):
+        _expect(name, t, o_sparse.shape[:3], torch.float32)
+    terms = torch.empty((B, H, 4), dtype=torch.float64, device=o_sparse.device)
+    tau = torch.empty(o_sparse.shape[:3], dtype=torch.float32, device=o_sparse.device) if with_tau else None
+    _lib.check("spa2_error_terms", _lib.lib().spa2_error_terms(
+        C.byref(_desc(o_sparse, bq, bkv)), _ptr(o_sparse), _ptr(lse_sparse), _ptr(o_dense),
+        _ptr(lse_dense), _ptr(terms), _ptr(tau), _stream(o_sparse)))
+    return (terms, tau) if with_tau else terms

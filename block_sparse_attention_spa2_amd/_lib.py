@@ -41,6 +41,7 @@ SIGNATURES = {
     "spa2_bwd_prep": (C.c_int, [_DESC, _P, _P, _P, _P, _P]),
     "spa2_bwd_dkdv": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P]),
     "spa2_bwd_dq": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _BM, _P, _P]),
+    "spa2_error_terms": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P]),
     "spa2_bwd_dq_rowterm": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P]),
 }
 

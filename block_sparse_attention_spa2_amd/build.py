@@ -25,7 +25,7 @@ FLAGS = [
     # no packed fp32 ALU ops in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-SOURCES = ["mask.hip", "fwd.hip", "bwd.hip", "api.cpp"]
+SOURCES = ["mask.hip", "fwd.hip", "bwd.hip", "diag.hip", "api.cpp"]
 
 
 def _compile(src: str) -> str:

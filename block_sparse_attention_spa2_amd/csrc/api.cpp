@@ -227,6 +227,18 @@ spa2_status spa2_bwd_dq_rowterm(const spa2_desc* desc, const void* q, const void
                                      dvec, spa2::kBwdDqRow, (hipStream_t)stream));
 }
 
+spa2_status spa2_error_terms(const spa2_desc* desc, const float* o_sparse, const float* lse_sparse,
+                             const float* o_dense, const float* lse_dense, double* terms,
+                             float* tau, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!o_sparse || !lse_sparse || !o_dense || !lse_dense || !terms) return SPA2_E_NULL;
+  return hip_status("error_terms",
+                    spa2::launch_error_terms(s, o_sparse, lse_sparse, o_dense, lse_dense, terms,
+                                             tau, (hipStream_t)stream));
+}
+
 spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f32,
                           const void* dout, float* dvec, void* stream) {
   spa2::Shape s;

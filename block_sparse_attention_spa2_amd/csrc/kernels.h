@@ -33,6 +33,9 @@ hipError_t launch_cols(const Shape& s, const spa2_blockmask& m, hipStream_t st);
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const int32_t* row_cnt, const int32_t* row_idx, const int32_t* row_order,
                       void* o, float* lse, float* o_f32, hipStream_t st);
+hipError_t launch_error_terms(const Shape& s, const float* os, const float* ls, const float* od,
+                              const float* ld, double* terms, float* tau, hipStream_t st);
+
 // stage bits for launch_bwd
 // kBwdDqRow: the dQ pass that also computes the row term (instead of kBwdPrep), run
 // before the dK/dV pass.

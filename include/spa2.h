@@ -177,6 +177,26 @@ spa2_status spa2_bwd_dq(const spa2_desc* desc, const void* q, const void* k, con
                         const float* lse, const void* dout, const float* dvec,
                         const spa2_blockmask* m, void* dq, void* stream);
 
+/* Error decomposition of the sparse output against the dense one (rainbus summary,
+ * "技术新颖性": with p the dense attention weights, m the kept-key mask and
+ * tau = sum(p * m) the dense mass on kept keys of a row,
+ *   O_dense - O_sparse = (p * (1 - m)) V + (1 - 1/tau) (p * m) V,
+ * the first term being the dropped mass, the second the renormalisation of the kept
+ * weights). Since (p * m) V = tau O_sparse and tau = exp(LSE_sparse - LSE_dense), both
+ * terms follow from the two forwards' outputs:
+ *   dropped = O_dense - tau O_sparse,   renormalisation = (tau - 1) O_sparse.
+ * o_sparse, o_dense: float [B, H, N, D] (the o_f32 outputs of spa2_fwd with the mask and
+ * with m = NULL); lse_sparse, lse_dense: float [B, H, N]. A row with no kept key has
+ * tau = 0. Writes terms[B, H, 4] (double, device), per head:
+ *   [0] sum |O_dense|, [1] sum |O_dense - O_sparse|, [2] sum |dropped|,
+ *   [3] sum |renormalisation|   (sums over the head's N x D elements; relative L1 errors
+ *   are [1]/[0], [2]/[0], [3]/[0]),
+ * and, if tau is not NULL, tau[B, H, N] (float, device). Sums are accumulated in double
+ * with atomic adds, so the last bits may vary between runs. */
+spa2_status spa2_error_terms(const spa2_desc* desc, const float* o_sparse, const float* lse_sparse,
+                             const float* o_dense, const float* lse_dense, double* terms,
+                             float* tau, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,7 @@ from .spa2_oracle import (  # noqa: F401
     block_mask,
     attn_fwd_head,
     attn_fwd,
+    error_terms_head,
     attn_bwd_head,
     attn_bwd,
 )

@@ -225,6 +225,27 @@ def attn_fwd(q, k, v, mask, bq: int, bkv: int):
 
 
 # ---------------------------------------------------------------------------------------
+# Error decomposition  ([rainbus] 技术新颖性: O_dense - O_sparse = (p (1-m)) V +
+#   (1 - 1/tau)(p m) V, p the dense weights, m the kept-key mask, tau the dense mass on
+#   the kept keys). From the two forwards: tau = exp(LSE_sparse - LSE_dense) (0 for a row
+#   with no kept key), (p m) V = tau O_sparse, so the terms are O_dense - tau O_sparse
+#   (dropped mass) and (tau - 1) O_sparse (renormalisation).
+# ---------------------------------------------------------------------------------------
+def error_terms_head(o_sparse, lse_sparse, o_dense, lse_dense):
+    """Per head: (sum |O_dense|, sum |O_dense - O_sparse|, sum |dropped|, sum |renorm|),
+    and tau [N]."""
+    o_s = np.asarray(o_sparse, np.float64)
+    o_d = np.asarray(o_dense, np.float64)
+    ls = np.asarray(lse_sparse, np.float64)
+    ld = np.asarray(lse_dense, np.float64)
+    tau = np.where(np.isneginf(ls), 0.0, np.exp(ls - ld))
+    t = tau[:, None]
+    sums = (np.abs(o_d).sum(), np.abs(o_d - o_s).sum(), np.abs(o_d - t * o_s).sum(),
+            np.abs((t - 1.0) * o_s).sum())
+    return np.array(sums), tau
+
+
+# ---------------------------------------------------------------------------------------
 # Backward ([rainbus] 核心方法 and [abstract]: the sparse attention is trainable, with a
 # forward and a backward pass). The pages give no backward formulas; these are the
 # derivatives of the forward above with the mask held fixed:

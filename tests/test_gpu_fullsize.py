@@ -8,7 +8,11 @@ import numpy as np
 import pytest
 import torch
 
+import json
+import os
+
 import block_sparse_attention_spa2_amd as spa2
+from block_sparse_attention_spa2_amd.calibrate import calibrate
 import oracle
 from gen import configs
 from tests import gpu_util as gu
@@ -92,6 +96,20 @@ def test_staged_backward_equals_bwd(wan13b):
         rel = ((a - b).norm() / a.norm()).item()
         print(f"[wan13b_480p] {nm}: separate row-term pass vs fused, rel L2 {rel:.2e}")
         assert rel <= 1e-3, (nm, rel)
+
+
+def test_wan13b_calibration_matches_oracle(wan13b):
+    """GPU bisection for 5% kept pairs at k = 2% lands on the step the oracle-only script
+    found (tests/golden/calibrated_p.json): same count, same flat interval."""
+    d = wan13b["dev"]
+    with open(os.path.join(os.path.dirname(__file__), "golden", "calibrated_p.json")) as f:
+        golden = json.load(f)["wan13b_480p"]
+    cal = calibrate(d["q"], d["k"], golden["k"], 0.05)
+    print(f"[wan13b_480p] calibrated p={cal.p!r} kept {cal.kept_pairs} interval {cal.interval}")
+    assert cal.kept_pairs == golden["kept_pairs"]
+    lo, hi = golden["interval"]
+    assert abs(cal.interval[0] - lo) < 1e-11 and abs(cal.interval[1] - hi) < 1e-11
+    assert lo < cal.p < hi
 
 
 @pytest.fixture(scope="module")

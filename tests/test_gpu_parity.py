@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import block_sparse_attention_spa2_amd as spa2
+from block_sparse_attention_spa2_amd.calibrate import calibrate
 import oracle
 from gen import configs, synth
 from tests import gpu_util as gu
@@ -346,3 +347,57 @@ def test_schedule_order(name):
     g2 = spa2.bwd(d["q"], d["k"], d["v"], o2, l2, d["do"], natural, o_f32=of2)
     for a_, b_ in zip(g1, g2):
         assert torch.equal(a_, b_)
+
+
+def test_calibrate_per_head():
+    """Per-head Top-p calibration on the GPU: at each returned p the oracle keeps the same
+    number of blocks as the GPU, and no neighbouring step of the oracle's count is nearer
+    the target."""
+    r = ref("mid_bf16")
+    d, inp = r["dev"], r["inp"]
+    target = 0.12
+    cals = calibrate(d["q"], d["k"], r["k"], target, r["bq"], r["bkv"], per_head=True)
+    assert len(cals) == d["q"].shape[0] * d["q"].shape[1]
+    for hh in (0, 5):
+        c = cals[hh]
+        pb = r["infos"][hh]["pbar"]
+        cnt = lambda p: sum(len(oracle.select_row(pb[i], r["k"], p)["kept"]) for i in range(pb.shape[0]))
+        want = target * pb.size
+        assert cnt(c.p) == c.kept_pairs
+        lo, hi = c.interval
+        below, above = cnt(lo - 1e-9), cnt(hi + 1e-9)
+        if lo > 1e-9:
+            assert below < c.kept_pairs
+        if hi < 1.0 - 1e-9:
+            assert above > c.kept_pairs
+        assert abs(c.kept_pairs - want) <= abs(below - want)
+        assert abs(c.kept_pairs - want) <= abs(above - want)
+        print(f"[mid_bf16 head {hh}] p={c.p:.9f} kept {c.kept_fraction:.4f} (target {target})")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "ragged_bf16", "ragged_bf16_d64"])
+def test_error_terms(name):
+    """Error decomposition kernel: GPU sparse and dense forwards -> spa2_error_terms, against
+    the oracle's sparse and dense forwards -> error_terms_head, per head."""
+    r = ref(name)
+    d, inp = r["dev"], r["inp"]
+    bm = _oracle_bm(r)
+    os32 = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    od32 = torch.empty_like(os32)
+    _, ls = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=os32)
+    _, ld = spa2.fwd(d["q"], d["k"], d["v"], None, r["bq"], r["bkv"], o_f32=od32)
+    terms, tau = spa2.error_terms(os32, ls, od32, ld, r["bq"], r["bkv"], with_tau=True)
+    terms, tau = terms.cpu().numpy(), tau.cpu().numpy()
+    q, kk, v = (inp.f64(x) for x in ("q", "k", "v"))
+    full = np.ones_like(r["mask"])
+    o_d, l_d = oracle.attn_fwd(q, kk, v, full, r["bq"], r["bkv"])
+    rtol, ttol = (1e-4, 1e-5) if inp.dtype == "f32" else (2e-2, 2e-3)
+    B, H = q.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            want, t = oracle.error_terms_head(r["o"][b, h], r["lse"][b, h], o_d[b, h], l_d[b, h])
+            np.testing.assert_allclose(terms[b, h], want, rtol=rtol)
+            assert np.abs(tau[b, h] - t).max() <= ttol
+    print(f"[{name}] rel L1 {terms[..., 1].sum() / terms[..., 0].sum():.4f} = dropped "
+          f"{terms[..., 2].sum() / terms[..., 0].sum():.4f} + renorm "
+          f"{terms[..., 3].sum() / terms[..., 0].sum():.4f} (triangle)")

@@ -248,6 +248,29 @@ def test_error_decomposition_closed_form():
     np.testing.assert_allclose(o_sp, (pd * tok) @ v / tau, rtol=0, atol=1e-12)
 
 
+def test_error_terms_against_definition():
+    """error_terms_head, which works from the two forwards' outputs only, equals the sums of
+    the decomposition's terms built from the dense weights p and the token mask m; an empty
+    row (tau = 0) puts its whole dense output into the dropped term."""
+    n, bq, bkv = 300, 64, 32
+    q, k, v, _, mask = _case(12, n=n, bq=bq, bkv=bkv)
+    mask[2] = False  # rows 128..191 keep nothing
+    tok = _token_mask(mask, n, bq, bkv).astype(np.float64)
+    pd = torch.softmax(torch.from_numpy(q @ k.T / 4.0), dim=1).numpy()
+    tau = (pd * tok).sum(axis=1, keepdims=True)
+    dropped = (pd * (1 - tok)) @ v
+    with np.errstate(divide="ignore", invalid="ignore"):
+        renorm = np.where(tau > 0, (1 - 1 / tau) * ((pd * tok) @ v), 0.0)
+    o_dense, lse_dense = oracle.attn_fwd_head(q, k, v, np.ones_like(mask), bq, bkv)
+    o_sp, lse_sp = oracle.attn_fwd_head(q, k, v, mask, bq, bkv)
+    sums, t = oracle.error_terms_head(o_sp, lse_sp, o_dense, lse_dense)
+    np.testing.assert_allclose(t, tau[:, 0], rtol=1e-12, atol=0)
+    want = [np.abs(o_dense).sum(), np.abs(o_dense - o_sp).sum(), np.abs(dropped).sum(),
+            np.abs(renorm).sum()]
+    np.testing.assert_allclose(sums, want, rtol=1e-11)
+    assert np.allclose(np.abs(dropped[128:192]).sum(), np.abs(o_dense[128:192]).sum(), rtol=1e-12)
+
+
 def test_empty_row_convention():
     q, k, v, do, mask = _case(5)
     mask[1] = False
