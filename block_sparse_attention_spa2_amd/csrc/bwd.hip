@@ -526,48 +526,52 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) l4[mt][e] *= kLog2e;
     }
-    // S[query 16 mt + 4 g + e][key 16 kt + c16], dP likewise
-    f32x4 s[MT][KT], dp[MT][KT];
+    // Two halves of the wave's rows (u): S, dP, P, dS of half u (scores), then the dV/dK
+    // products of half u; the products of half 0 are issued after the scores of half 1,
+    // which do not depend on them.
+    F pf[MT / 2][KT], sf[MT / 2][KT];
+    auto scores = [&](int u) __attribute__((always_inline)) {
+      f32x4 s[2][KT], dp[2][KT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        s[mt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[mt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const F qa = QTile::read_row8(Qb, qrow0 + mt * 16 + c16, ks * 32 + 8 * g);
-        const F da = QTile::read_row8(Db, qrow0 + mt * 16 + c16, ks * 32 + 8 * g);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-          s[mt][kt] = E::mma(qa, kf[kt][ks], s[mt][kt]);
-          dp[mt][kt] = E::mma(da, vf[kt][ks], dp[mt][kt]);
+          s[h][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int mt = 2 * u + h;
+          const F qa = QTile::read_row8(Qb, qrow0 + mt * 16 + c16, ks * 32 + 8 * g);
+          const F da = QTile::read_row8(Db, qrow0 + mt * 16 + c16, ks * 32 + 8 * g);
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            s[h][kt] = E::mma(qa, kf[kt][ks], s[h][kt]);
+            dp[h][kt] = E::mma(da, vf[kt][ks], dp[h][kt]);
+          }
         }
       }
-    }
-    // P (kept in s) and dS (kept in dp)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][kt][e], a.scale_log2, -l4[mt][e]));
-          s[mt][kt][e] = p;
-          dp[mt][kt][e] = p * (dp[mt][kt][e] - d4[mt][e]);
-        }
-    // dV^T += dO^T P ; dK^T += Q^T dS  (reduction over the wave's queries, 32 at a time)
-#pragma unroll
-    for (int u = 0; u < MT / 2; ++u) {
-      F pf[KT], sf[KT];
+          for (int e = 0; e < 4; ++e) {
+            const int mt = 2 * u + h;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][kt][e], a.scale_log2, -l4[mt][e]));
+            s[h][kt][e] = p;
+            dp[h][kt][e] = p * (dp[h][kt][e] - d4[mt][e]);
+          }
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        pf[kt] = E::pack(s[2 * u][kt], s[2 * u + 1][kt]);
-        sf[kt] = E::pack(dp[2 * u][kt], dp[2 * u + 1][kt]);
+        pf[u][kt] = E::pack(s[0][kt], s[1][kt]);
+        sf[u][kt] = E::pack(dp[0][kt], dp[1][kt]);
       }
+    };
+    // dV^T += dO^T P ; dK^T += Q^T dS over the 32 queries of half u
+    auto products = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         F dot, qtr;
@@ -577,11 +581,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
         QTile::read_col4(Qb, qrow0 + 32 * u + 16, dt * 16, qtr, 1);
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-          dv[dt][kt] = E::mma(dot, pf[kt], dv[dt][kt]);
-          dk[dt][kt] = E::mma(qtr, sf[kt], dk[dt][kt]);
+          dv[dt][kt] = E::mma(dot, pf[u][kt], dv[dt][kt]);
+          dk[dt][kt] = E::mma(qtr, sf[u][kt], dk[dt][kt]);
         }
       }
+    };
+    scores(0);
+#pragma unroll
+    for (int u = 1; u < MT / 2; ++u) {
+      scores(u);
+      products(u - 1);
     }
+    products(MT / 2 - 1);
   };
 
   if constexpr (NS == 2) {
