@@ -25,8 +25,8 @@ spa2_status check_desc(const spa2_desc* d, spa2::Shape* out) {
   if (d->B < 1 || d->H < 1 || d->N < 1 || d->N > (1 << 20)) return SPA2_E_SHAPE;
   if ((long long)d->B * d->H > (1LL << 24)) return SPA2_E_SHAPE;
   if (d->D != 64 && d->D != 128) return SPA2_E_SHAPE;
-  if (d->BQ != 64 && d->BQ != 128) return SPA2_E_SHAPE;
-  if (d->BKV != 64) return SPA2_E_SHAPE;
+  if (d->BQ != 64 && d->BQ != 128 && d->BQ != 256) return SPA2_E_SHAPE;
+  if (d->BKV != 32 && d->BKV != 64 && d->BKV != 128) return SPA2_E_SHAPE;
   const int tn = blocks(d->N, d->BKV);
   if (tn > spa2::kMaxTn) return SPA2_E_SHAPE;
   *out = spa2::Shape{d->B, d->H, d->N, d->D, d->BQ, d->BKV, d->dtype, blocks(d->N, d->BQ), tn};

@@ -17,6 +17,8 @@
 //             lists), like the forward; K_j and V_j are staged in LDS.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -41,6 +43,9 @@ struct BwdArgs {
   void* dv;
   float* dvec;
   int N, Tm, Tn, BH;
+  int bq_block, bkv_block;  // rows / keys of a mask block (multiples of the kernels' tiles)
+  int qsub, ksub;           // log2 of the query tiles per block and key tiles per key block
+                            // (the loops over lists take them as template parameters)
   int rowterm;  // dQ pass: compute Dv = rowsum(dO * O) itself and store it in dvec
   float scale_log2;  // log2(e) / sqrt(D)
   float scale;       // 1 / sqrt(D)
@@ -100,11 +105,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // pkc += C^T W'. The groups' partials of sum_k bf16(dS_k) come from the matrix unit too
 // (a 0/1 operand times the packed dS), so sum_k r_k costs one add per element.
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int BQ, bool DENSE, int NW>
+template <typename T, int D, int BQ, int BKV, int KSUB, bool DENSE, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int BKV = 64;
+  constexpr int KTN = BKV / 16;  // 16-key tiles per key step (BQ x BKV tiles)
+  constexpr int UPV = BKV / 32;  // 32-key reduction steps of the dQ product
   constexpr int QT = BQ / (16 * NW);  // 16-row query tiles per wave
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -124,8 +130,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pos = xcd_item(blockIdx.x, a.BH * a.Tm);
-  const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[pos]) : pos;
+  const int pos = xcd_item(blockIdx.x, (a.BH * a.Tm) << a.qsub);
+  const int ppos = pos >> a.qsub;  // this query tile's block, in scheduling order
+  const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[ppos]) : ppos;
   const int bh = item / a.Tm, qb = item % a.Tm;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
@@ -133,13 +140,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   const T* K = (const T*)a.k + head;
   const T* V = (const T*)a.v + head;
   const T* dO = (const T*)a.dout + head;
-  const int q0 = qb * BQ + w * 16 * QT;
+  const int q0 = qb * a.bq_block + (pos & ((1 << a.qsub) - 1)) * BQ + w * 16 * QT;
 
   constexpr bool dense = DENSE;
-  const int cnt = dense ? a.Tn : a.row_cnt[item];
-  BlockQueue<NS> bq;  // blocks t .. t + NS - 1 (tile loads) and t + NS (being read)
-  if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, cnt);
-  auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
+  const int cnt = dense ? (N + BKV - 1) / BKV : a.row_cnt[item] << KSUB;  // key steps
+  static_assert(NS <= 3, "TileQueue reads two positions ahead");
+  TileQueue<KSUB> bq;  // key tiles t .. t + NS - 1 (tile loads) and t + NS (being read)
+  if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, a.row_cnt[item]);
+  auto block_at = [&](int t, int i) { return dense ? t + i : bq.tile(t, i); };
   typename KV::template Plan<NW> plan;
   plan.init(w);
   auto issue = [&](char* stage, int j) {
@@ -276,9 +284,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
       }
     }
 
-    f32x4 s[4][QT], dp[4][QT];
+    f32x4 s[KTN][QT], dp[KTN][QT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < KTN; ++kt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -287,7 +295,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < KTN; ++kt) {
         const F ka = KV::read_row8(Kb, kt * 16 + c16, ks * 32 + 8 * g);
         const F va = KV::read_row8(Vb, kt * 16 + c16, ks * 32 + 8 * g);
 #pragma unroll
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     // keys past N exist only in the last, partial key block: P = 0 there
     if ((j + 1) * BKV > N) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KTN; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (j * BKV + kt * 16 + 4 * g + e >= N)
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) pb[qt] = tb[qt] = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < KTN; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) cs[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < UPV; ++u) {
       F pf[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
@@ -423,11 +431,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 //   dS = P * (dP - Dv), dV^T += dO^T P, dK^T += Q^T dS (A via transpose reads).
 // At the end the query groups' partial sums are added through LDS.
 // ------------------------------------------------------------------------------------
-template <typename T, int D, int BQ, bool DENSE, int NW, int KT>
+template <typename T, int D, int BQ, int BKV, int QSUB, bool DENSE, int NW, int KT>
 __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int BKV = 64;
   constexpr int KW = BKV / (16 * KT);    // key groups (KT 16-key tiles per wave)
   constexpr int QW = NW / KW;            // query groups
   constexpr int MT = BQ / QW / 16;       // 16-row query tiles per wave
@@ -446,8 +453,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = w % KW, qh = w / KW;
-  const int pos = xcd_item(blockIdx.x, a.BH * a.Tn);
-  const int item = a.col_order ? __builtin_amdgcn_readfirstlane(a.col_order[pos]) : pos;
+  const int pos = xcd_item(blockIdx.x, (a.BH * a.Tn) << a.ksub);
+  const int ppos = pos >> a.ksub;  // this key tile's block, in scheduling order
+  const int item = a.col_order ? __builtin_amdgcn_readfirstlane(a.col_order[ppos]) : ppos;
   const int bh = item / a.Tn, kb = item % a.Tn;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
@@ -457,14 +465,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
   const T* dO = (const T*)a.dout + head;
   const float* LSE = a.lse + (size_t)bh * N;
   const float* DV = a.dvec + (size_t)bh * N;
-  const int k0 = kb * BKV + kh * 16 * KT;  // first key of this wave
+  const int k0 = kb * a.bkv_block + (pos & ((1 << a.ksub) - 1)) * BKV + kh * 16 * KT;  // first key of this wave
   const int qrow0 = qh * (BQ / QW);        // first query row of this wave within a block
 
   constexpr bool dense = DENSE;
-  const int cnt = dense ? a.Tm : a.col_cnt[item];
-  BlockQueue<2> bq;  // query blocks t, t + 1 (next tile load) and t + 2 (being read)
-  if (!dense) bq.init(a.col_idx + (size_t)item * a.Tm, cnt);
-  auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
+  const int cnt = dense ? (N + BQ - 1) / BQ : a.col_cnt[item] << QSUB;  // query tiles
+  TileQueue<QSUB> bq;  // query tiles t, t + 1 (next tile load) and t + 2 (being read)
+  if (!dense) bq.init(a.col_idx + (size_t)item * a.Tm, a.col_cnt[item]);
+  auto block_at = [&](int t, int i) { return dense ? t + i : bq.tile(t, i); };
   typename QTile::template Plan<NW> plan;
   plan.init(w);
   auto issue = [&](char* stage, int i) {
@@ -679,6 +687,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
 // fp32 runs four waves of two tiles.
 template <typename T, int BQ>
 constexpr int dkdv_key_tiles() { return sizeof(T) == 2 ? 1 : 2; }
+// dK/dV waves: 2 x 16-row query tiles per wave at least (the products reduce over 32 rows)
+template <typename T, int BQ, int BKV>
+constexpr int dkdv_waves() {
+  return (sizeof(T) == 2 ? 8 : 4) / (BKV == 32 && BQ == 64 ? 2 : 1);
+}
+// dQ waves: 16 rows each (bf16), except with 32-key tiles at D = 64, where a K/V tile is only
+// four 1 KB loads (32 rows each then); fp32: four waves
+template <typename T, int D, int BQ, int BKV>
+constexpr int dq_waves() {
+  return sizeof(T) == 2 ? (D == 64 && BKV == 32 ? BQ / 32 : BQ / 16) : 4;
+}
 
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* o_f32, const float* lse, const void* dout, const spa2_blockmask* m, void* dq,
@@ -687,46 +706,51 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
             m ? m->row_cnt : nullptr, m ? m->row_idx : nullptr,
             m ? m->col_cnt : nullptr, m ? m->col_idx : nullptr,
             m ? m->row_order : nullptr, m ? m->col_order : nullptr,
-            dq, dk, dv, dvec, s.N, s.Tm, s.Tn, s.BH(), 0,
+            dq, dk, dv, dvec, s.N, s.Tm, s.Tn, s.BH(), s.BQ, s.BKV, s.qsub(), s.ksub(), 0,
             (float)(1.4426950408889634 / sqrt((double)s.D)), (float)(1.0 / sqrt((double)s.D))};
   const int tpr = s.D * (s.dtype == SPA2_BF16 ? 2 : 4) / 16;
   const int rpb = 256 / tpr;
   const size_t rows = (size_t)s.BH() * s.N;
   const dim3 gpre((unsigned)((rows + rpb - 1) / rpb));
-  const dim3 gq(s.BH() * s.Tm), gk(s.BH() * s.Tn);
-#define SPA2_BWD(T, D, BQ)                                                       \
-  do {                                                                           \
-    constexpr int nq = sizeof(T) == 2 ? BQ / 16 : 4;                            \
-    if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);        \
-    if (stages & kBwdDqRow) { /* dQ and the row term first: dK/dV reads dvec */  \
-      a.rowterm = 1;                                                             \
-      if (m) bwd_dq_kernel<T, D, BQ, false, nq><<<gq, 64 * nq, 0, st>>>(a);     \
-      else bwd_dq_kernel<T, D, BQ, true, nq><<<gq, 64 * nq, 0, st>>>(a);        \
-      a.rowterm = 0;                                                             \
-    }                                                                            \
-    if (stages & kBwdDkdv) {                                                     \
-      constexpr int nw = sizeof(T) == 2 ? 8 : 4, kt = dkdv_key_tiles<T, BQ>(); \
-      if (m) bwd_dkdv_kernel<T, D, BQ, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
-      else bwd_dkdv_kernel<T, D, BQ, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a);    \
-    }                                                                            \
-    if (stages & kBwdDq) {                                                       \
-      if (m) bwd_dq_kernel<T, D, BQ, false, nq><<<gq, 64 * nq, 0, st>>>(a);     \
-      else bwd_dq_kernel<T, D, BQ, true, nq><<<gq, 64 * nq, 0, st>>>(a);        \
-    }                                                                            \
+  const dim3 gq((s.BH() * s.Tm) << s.qsub()), gk((s.BH() * s.Tn) << s.ksub());
+#define SPA2_BWD(T, D, BQ, BK)                                                       \
+  do {                                                                               \
+    constexpr int nq = dq_waves<T, D, BQ, BK>();                                     \
+    auto launch_dq = [&](auto nqt) {                                                 \
+      constexpr int NQ = decltype(nqt)::value;                                       \
+      if (!m) bwd_dq_kernel<T, D, BQ, BK, 0, true, NQ><<<gq, 64 * NQ, 0, st>>>(a);  \
+      else if (s.ksub()) bwd_dq_kernel<T, D, BQ, BK, 1, false, NQ><<<gq, 64 * NQ, 0, st>>>(a); \
+      else bwd_dq_kernel<T, D, BQ, BK, 0, false, NQ><<<gq, 64 * NQ, 0, st>>>(a);    \
+    };                                                                               \
+    if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);            \
+    if (stages & kBwdDqRow) { /* dQ and the row term first: dK/dV reads dvec */      \
+      a.rowterm = 1;                                                                 \
+      launch_dq(std::integral_constant<int, nq>{});                                  \
+      a.rowterm = 0;                                                                 \
+    }                                                                                \
+    if (stages & kBwdDkdv) {                                                         \
+      constexpr int nw = dkdv_waves<T, BQ, BK>(), kt = dkdv_key_tiles<T, BQ>();      \
+      if (!m) bwd_dkdv_kernel<T, D, BQ, BK, 0, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+      else if (s.qsub()) bwd_dkdv_kernel<T, D, BQ, BK, 1, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+      else bwd_dkdv_kernel<T, D, BQ, BK, 0, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+    }                                                                                \
+    if (stages & kBwdDq) launch_dq(std::integral_constant<int, nq>{});               \
+  } while (0)
+#define SPA2_BWD_BK(T, D, BQ)                                                        \
+  do {                                                                               \
+    if (s.bkv_tile() == 32) SPA2_BWD(T, D, BQ, 32); else SPA2_BWD(T, D, BQ, 64);     \
+  } while (0)
+#define SPA2_BWD_BQ(T, D)                                                            \
+  do {                                                                               \
+    if (s.bq_tile() == 64) SPA2_BWD_BK(T, D, 64); else SPA2_BWD_BK(T, D, 128);       \
   } while (0)
   if (s.dtype == SPA2_BF16) {
-    if (s.D == 64) {
-      if (s.BQ == 64) SPA2_BWD(bf16, 64, 64); else SPA2_BWD(bf16, 64, 128);
-    } else {
-      if (s.BQ == 64) SPA2_BWD(bf16, 128, 64); else SPA2_BWD(bf16, 128, 128);
-    }
+    if (s.D == 64) SPA2_BWD_BQ(bf16, 64); else SPA2_BWD_BQ(bf16, 128);
   } else {
-    if (s.D == 64) {
-      if (s.BQ == 64) SPA2_BWD(float, 64, 64); else SPA2_BWD(float, 64, 128);
-    } else {
-      if (s.BQ == 64) SPA2_BWD(float, 128, 64); else SPA2_BWD(float, 128, 128);
-    }
+    if (s.D == 64) SPA2_BWD_BQ(float, 64); else SPA2_BWD_BQ(float, 128);
   }
+#undef SPA2_BWD_BQ
+#undef SPA2_BWD_BK
 #undef SPA2_BWD
   return hipGetLastError();
 }

@@ -89,6 +89,30 @@ struct BlockQueue {
   }
 };
 
+// Tiles of a kept-block list when every kept block covers 2^S consecutive tiles of the
+// kernel (S = 0 or 1; S = 1 for 128-key blocks run as two 64-key tiles, or 256-row blocks
+// as two 128-row tiles): tile t is sub-tile (t mod 2^S) of list entry t >> S. tile(t, i)
+// is the tile at position t + i (i <= 2; entries past the list read as block 0);
+// advance(t) moves from t to t + 1. t must be wave-uniform. S is a template parameter so
+// that the plain case (S = 0) is exactly BlockQueue, with no branch in the loop.
+template <int S>
+struct TileQueue {
+  BlockQueue<2> bq;
+  __device__ __forceinline__ void init(const int32_t* l, int blocks) { bq.init(l, blocks); }
+  __device__ __forceinline__ int tile(int t, int i) const {
+    if constexpr (S == 0) {
+      return bq.q[i];
+    } else {
+      const int u = (t & 1) + i;
+      return (bq.q[u >> 1] << 1) + (u & 1);
+    }
+  }
+  __device__ __forceinline__ void advance(int t) {
+    if constexpr (S == 0) bq.advance(t);
+    else if (t & 1) bq.advance(t >> 1);
+  }
+};
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained): this wave's outstanding
 // vector memory operations, including direct-to-LDS loads, have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0xF70); }
@@ -245,6 +269,7 @@ struct Tile {
   template <int NW>
   struct Plan {
     static constexpr int kLoads = kChunks * ROWS / 64 / NW;  // loads per wave per tile
+    static_assert(kLoads * NW * 64 == kChunks * ROWS, "every wave issues the same loads");
     int off[kLoads];
     __device__ __forceinline__ void init(int wave) {
       const int l = lane_id();

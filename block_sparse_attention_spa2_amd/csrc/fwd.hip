@@ -34,45 +34,54 @@ struct FwdArgs {
   const int32_t* row_cnt;  // nullptr: dense
   const int32_t* row_idx;
   const int32_t* row_order;  // optional scheduling order of the query blocks
-  int N, Tm, Tn, items;
+  int N, Tm, Tn, items;  // items: workgroups = query blocks x query tiles per block
+  int bq_block;          // rows of a mask query block (a multiple of the kernel's tile)
+  int qsub;              // log2 of the query tiles per block
   float scale_log2;  // log2(e) / sqrt(D)
 };
 
 // Rescale threshold in log2 units: probabilities stay below 2^8 between rescales.
 constexpr float kRescaleSlack = 8.0f;
 
-template <typename T, int D, int BQ, bool DENSE, int NW>
+// Tiles: BQ query rows per workgroup, BKV keys per step (32 or 64). A mask block of 256
+// rows runs as two workgroups (query tiles), a 128-key block as two key steps.
+template <typename T, int D, int BQ, int BKV, int KSUB, bool DENSE, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
-  constexpr int BKV = 64;
   constexpr int QT = BQ / (16 * NW);  // 16-row query tiles per wave
   constexpr int KS = D / 32;   // reduction steps over the head dimension
   constexpr int DT = D / 16;   // 16-wide output column tiles
+  constexpr int KTN = BKV / 16;  // 16-key score tiles per step
+  constexpr int UPV = BKV / 32;  // 32-key reduction steps of O^T += V^T P^T
   using KV = Tile<T, BKV, D>;
   // Two stages in two separate LDS variables: every access names one of them statically
   // (the loop below is unrolled by two), so the compiler can tell that the loads into one
   // stage do not alias the reads of the other and does not wait for them early.
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * KV::kBytes];
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * KV::kBytes];
+  // the epilogue stages half the fp32 O tile in each stage
+  constexpr int kStageBytes = 2 * KV::kBytes > BQ / 2 * D * 4 ? 2 * KV::kBytes : BQ / 2 * D * 4;
+  __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char stage1[kStageBytes];
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pos = xcd_item(blockIdx.x, a.items);
-  const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[pos]) : pos;
+  const int ppos = pos >> a.qsub;  // this query tile's block, in scheduling order
+  const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[ppos]) : ppos;
   const int bh = item / a.Tm, qb = item % a.Tm;
   const int N = a.N;
   const size_t head = (size_t)bh * N * D;
   const T* Q = (const T*)a.q + head;
   const T* K = (const T*)a.k + head;
   const T* V = (const T*)a.v + head;
-  const int q0 = qb * BQ + w * 16 * QT;
+  const int r0 = qb * a.bq_block + (pos & ((1 << a.qsub) - 1)) * BQ;  // first row of the tile
+  const int q0 = r0 + w * 16 * QT;
 
-  constexpr bool dense = DENSE;  // dense: every key block, no list
-  const int cnt = dense ? a.Tn : a.row_cnt[item];
-  BlockQueue<2> bq;  // blocks t, t + 1 (next tile load) and t + 2 (being read)
-  if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, cnt);
-  auto block_at = [&](int t, int i) { return dense ? t + i : bq.q[i]; };
+  constexpr bool dense = DENSE;  // dense: every key tile, no list
+  const int cnt = dense ? (N + BKV - 1) / BKV : a.row_cnt[item] << KSUB;  // key steps
+  TileQueue<KSUB> bq;  // key tiles t, t + 1 (next tile load) and t + 2 (being read)
+  if (!dense) bq.init(a.row_idx + (size_t)item * a.Tn, a.row_cnt[item]);
+  auto block_at = [&](int t, int i) { return dense ? t + i : bq.tile(t, i); };
   typename KV::template Plan<NW> plan;
   plan.init(w);
   auto issue = [&](char* stage, int j) {
@@ -114,15 +123,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     const char* Vb = stage + KV::kBytes;
 
     // S^T = K Q^T : s[kt][qt] lane holds S^T[key 16 kt + 4 g + e][query 16 qt + c16]
-    f32x4 s[4][QT];
+    f32x4 s[KTN][QT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < KTN; ++kt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < KTN; ++kt) {
         const F ka = KV::read_row8(Kb, kt * 16 + c16, ks * 32 + 8 * g);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) s[kt][qt] = E::mma(ka, qf[qt][ks], s[kt][qt]);
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     // keys past N exist only in the last, partial key block
     if ((j + 1) * BKV > N) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KTN; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (j * BKV + kt * 16 + 4 * g + e >= N)
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     for (int qt = 0; qt < QT; ++qt) {
       float m = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KTN; ++kt)
         m = fmaxf(m, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
       mx[qt] = max4(m) * a.scale_log2;
       raise |= mx[qt] > mrow[qt] + kRescaleSlack;
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
       const float mref = mrow[qt] == -INFINITY ? 0.f : mrow[qt];
       float ls = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KTN; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][e], a.scale_log2, -mref));
@@ -177,9 +186,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
       lrow[qt] += ls;
     }
 
-    // O^T += V^T P^T over the block's 64 keys, 32 at a time
+    // O^T += V^T P^T over the step's keys, 32 at a time
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < UPV; ++u) {
       F pf[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) pf[qt] = E::pack(s[2 * u][qt], s[2 * u + 1][qt]);
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
   float* lse = a.lse + (size_t)bh * N;
   constexpr int kRowChunks = D / 4;               // 16-byte fp32 chunks per row
   constexpr int kHalfRows = BQ / 2;
-  static_assert(kHalfRows * D * 4 <= 2 * KV::kBytes, "a stage holds half of the O tile");
+  static_assert(kHalfRows * D * 4 <= kStageBytes, "a stage holds half of the O tile");
   auto chunk_at = [&](int r, int c) -> f32x4* {  // row r of the block, chunk c
     char* base = r < kHalfRows ? stage0 : stage1;
     const int rr = r % kHalfRows;
@@ -216,7 +225,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int rl = w * 16 * QT + qt * 16 + c16;  // row within the block
-    const int row = qb * BQ + rl;
+    const int row = r0 + rl;
     const float lt = sum4(lrow[qt]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
@@ -224,8 +233,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     if (g == 0 && row < N) lse[row] = lt > 0.f ? (mrow[qt] + __log2f(lt)) * kLn2 : -INFINITY;
   }
   lds_barrier();
-  const int rows_here = min(BQ, N - qb * BQ);
-  T* O = (T*)a.o + head + (size_t)qb * BQ * D;
+  const int rows_here = min(BQ, N - r0);
+  T* O = (T*)a.o + head + (size_t)r0 * D;
   constexpr int kEpc = 16 / (int)sizeof(T);        // elements per 16-byte output chunk
   constexpr int kOutChunks = BQ * D / kEpc;
   for (int f = tid; f < kOutChunks; f += 64 * NW) {
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     }
   }
   if (a.o_f32) {
-    float* Of = a.o_f32 + head + (size_t)qb * BQ * D;
+    float* Of = a.o_f32 + head + (size_t)r0 * D;
     for (int f = tid; f < BQ * kRowChunks; f += 64 * NW) {
       const int r = f / kRowChunks, c = f % kRowChunks;
       if (r >= rows_here) break;
@@ -264,29 +273,33 @@ constexpr int fwd_waves() { return 4; }
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const int32_t* row_cnt, const int32_t* row_idx, const int32_t* row_order,
                       void* o, float* lse, float* o_f32, hipStream_t st) {
+  const int items = (s.BH() * s.Tm) << s.qsub();
   FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, row_cnt ? row_order : nullptr, s.N, s.Tm,
-            s.Tn, s.BH() * s.Tm,
+            s.Tn, items, s.BQ, s.qsub(),
             (float)(1.4426950408889634 / sqrt((double)s.D))};
-  const dim3 grid(s.BH() * s.Tm);
-#define SPA2_FWD(T, D, BQ)                                               \
-  do {                                                                   \
-    constexpr int nw = fwd_waves<T, BQ>();                               \
-    if (row_cnt) fwd_kernel<T, D, BQ, false, nw><<<grid, 64 * nw, 0, st>>>(a); \
-    else fwd_kernel<T, D, BQ, true, nw><<<grid, 64 * nw, 0, st>>>(a);    \
+  const dim3 grid(items);
+#define SPA2_FWD(T, D, BQ, BK)                                                   \
+  do {                                                                           \
+    constexpr int nw = fwd_waves<T, BQ>();                                       \
+    if (!row_cnt) fwd_kernel<T, D, BQ, BK, 0, true, nw><<<grid, 64 * nw, 0, st>>>(a); \
+    else if (s.ksub()) fwd_kernel<T, D, BQ, BK, 1, false, nw><<<grid, 64 * nw, 0, st>>>(a); \
+    else fwd_kernel<T, D, BQ, BK, 0, false, nw><<<grid, 64 * nw, 0, st>>>(a);   \
+  } while (0)
+#define SPA2_FWD_BK(T, D, BQ)                                                    \
+  do {                                                                           \
+    if (s.bkv_tile() == 32) SPA2_FWD(T, D, BQ, 32); else SPA2_FWD(T, D, BQ, 64); \
+  } while (0)
+#define SPA2_FWD_BQ(T, D)                                                        \
+  do {                                                                           \
+    if (s.bq_tile() == 64) SPA2_FWD_BK(T, D, 64); else SPA2_FWD_BK(T, D, 128);   \
   } while (0)
   if (s.dtype == SPA2_BF16) {
-    if (s.D == 64) {
-      if (s.BQ == 64) SPA2_FWD(bf16, 64, 64); else SPA2_FWD(bf16, 64, 128);
-    } else {
-      if (s.BQ == 64) SPA2_FWD(bf16, 128, 64); else SPA2_FWD(bf16, 128, 128);
-    }
+    if (s.D == 64) SPA2_FWD_BQ(bf16, 64); else SPA2_FWD_BQ(bf16, 128);
   } else {
-    if (s.D == 64) {
-      if (s.BQ == 64) SPA2_FWD(float, 64, 64); else SPA2_FWD(float, 64, 128);
-    } else {
-      if (s.BQ == 64) SPA2_FWD(float, 128, 64); else SPA2_FWD(float, 128, 128);
-    }
+    if (s.D == 64) SPA2_FWD_BQ(float, 64); else SPA2_FWD_BQ(float, 128);
   }
+#undef SPA2_FWD_BQ
+#undef SPA2_FWD_BK
 #undef SPA2_FWD
   return hipGetLastError();
 }

@@ -12,6 +12,12 @@ struct Shape {
   int B, H, N, D, BQ, BKV, dtype;
   int Tm, Tn;   // query / key block counts
   int BH() const { return B * H; }
+  // The attention kernels work on tiles of at most 128 query rows and 64 keys; a larger
+  // mask block (BQ = 256, BKV = 128) is two consecutive tiles.
+  int bq_tile() const { return BQ > 128 ? 128 : BQ; }
+  int bkv_tile() const { return BKV > 64 ? 64 : BKV; }
+  int qsub() const { return BQ > 128 ? 1 : 0; }  // log2(BQ / bq_tile())
+  int ksub() const { return BKV > 64 ? 1 : 0; }  // log2(BKV / bkv_tile())
 };
 
 // Largest key-block count per row: the selection kernel holds a row in registers, 64 blocks

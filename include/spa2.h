@@ -24,8 +24,12 @@
  *   - Every argument is validated before any HIP call; an invalid call returns its error
  *     code and writes nothing. A failed kernel launch returns SPA2_E_HIP (details from
  *     spa2_last_error()). No C++ exception crosses this boundary.
- *   - Supported: dtype F32 or BF16, D in {64, 128}, BQ in {64, 128}, BKV = 64,
- *     1 <= N <= 2^20, B*H >= 1, T_n <= 4096.
+ *   - Supported: dtype F32 or BF16, D in {64, 128}, BQ in {64, 128, 256},
+ *     BKV in {32, 64, 128}, 1 <= N <= 2^20, B*H >= 1, T_n <= 4096. The method's sizes
+ *     are BQ = 128, BKV = 64; the others are the block-size variants the pages suggest
+ *     trying (rainbus summary, "局限与改进": fixed block sizes are a limitation). The
+ *     attention kernels work on tiles of at most 128 rows and 64 keys, so a 256-row or
+ *     128-key block is processed as two tiles (same result, same lists).
  *   - Attention is non-causal; the scale is 1/sqrt(D); LSE is the natural-log
  *     log-sum-exp of the scaled scores over the kept keys. Outputs are rounded to the
  *     input dtype (round to nearest even) from fp32 accumulators. A query row whose

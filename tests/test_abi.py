@@ -62,8 +62,10 @@ def test_status_strings():
 @pytest.mark.parametrize("kw,code", [
     (dict(N=0), _lib.E_SHAPE), (dict(N=(1 << 20) + 1), _lib.E_SHAPE), (dict(B=0), _lib.E_SHAPE),
     (dict(H=-1), _lib.E_SHAPE), (dict(D=96), _lib.E_SHAPE), (dict(D=256), _lib.E_SHAPE),
-    (dict(BQ=32), _lib.E_SHAPE), (dict(BQ=256), _lib.E_SHAPE), (dict(BKV=128), _lib.E_SHAPE),
-    (dict(N=4096 * 64 + 1), _lib.E_SHAPE), (dict(dtype=7), _lib.E_DTYPE),
+    (dict(BQ=32), _lib.E_SHAPE), (dict(BQ=512), _lib.E_SHAPE), (dict(BQ=96), _lib.E_SHAPE),
+    (dict(BKV=16), _lib.E_SHAPE), (dict(BKV=256), _lib.E_SHAPE), (dict(BKV=48), _lib.E_SHAPE),
+    (dict(N=4096 * 64 + 1), _lib.E_SHAPE), (dict(N=4096 * 32 + 1, BKV=32), _lib.E_SHAPE),
+    (dict(dtype=7), _lib.E_DTYPE),
 ])
 def test_bad_desc(kw, code):
     assert mask_call(desc=good(**kw)) == code
@@ -158,3 +160,16 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+@pytest.mark.parametrize("bq,bkv", [(64, 32), (64, 128), (128, 32), (128, 128), (256, 32),
+                                    (256, 64), (256, 128)])
+def test_block_size_variants_accepted(bq, bkv):
+    """Every b_q in {64, 128, 256} and b_kv in {32, 64, 128} passes validation (checked
+    through the workspace-size calls, which launch nothing)."""
+    L = _lib.lib()
+    n = C.c_size_t(0)
+    d = good(BQ=bq, BKV=bkv)
+    assert L.spa2_mask_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
+    assert n.value > 0
+    assert L.spa2_bwd_workspace_size(C.byref(d), C.byref(n)) == _lib.OK

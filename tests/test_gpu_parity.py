@@ -26,20 +26,31 @@ def _case(name):
         w = configs.params("mid_bf16")
         return configs.make_inputs("mid_bf16"), w["BQ"], w["BKV"], w["k"], w["p"]
     spec = {
-        # name: (B, H, N, D, BQ, dtype, seed, k, p)
-        "ragged_bf16": (2, 2, 1000, 128, 128, "bf16", 11, 0.10, 0.50),
-        "ragged_bf16_d64": (1, 3, 777, 64, 64, "bf16", 12, 0.15, 0.40),
-        "ragged_f32_d128": (1, 2, 600, 128, 128, "f32", 13, 0.20, 0.50),
-        "ragged_f32_d64_bq128": (1, 2, 700, 64, 128, "f32", 14, 0.20, 0.30),
-        "single_block": (1, 2, 50, 64, 64, "bf16", 15, 0.50, 0.50),
-        "one_row": (1, 1, 1, 128, 128, "bf16", 16, 0.50, 0.50),
+        # name: (B, H, N, D, BQ, BKV, dtype, seed, k, p)
+        "ragged_bf16": (2, 2, 1000, 128, 128, 64, "bf16", 11, 0.10, 0.50),
+        "ragged_bf16_d64": (1, 3, 777, 64, 64, 64, "bf16", 12, 0.15, 0.40),
+        "ragged_f32_d128": (1, 2, 600, 128, 128, 64, "f32", 13, 0.20, 0.50),
+        "ragged_f32_d64_bq128": (1, 2, 700, 64, 128, 64, "f32", 14, 0.20, 0.30),
+        "single_block": (1, 2, 50, 64, 64, 64, "bf16", 15, 0.50, 0.50),
+        "one_row": (1, 1, 1, 128, 128, 64, "bf16", 16, 0.50, 0.50),
+        # block-size variants (b_q 256 and b_kv 128 run as two kernel tiles; b_kv 32 has
+        # its own tile); ragged so that a second tile of the last block is partial or empty
+        "bkv32_bf16": (1, 2, 1000, 128, 128, 32, "bf16", 21, 0.10, 0.50),
+        "bkv128_bf16": (1, 2, 1000, 128, 128, 128, "bf16", 22, 0.15, 0.50),
+        "bq256_bf16": (1, 2, 1000, 128, 256, 64, "bf16", 23, 0.10, 0.50),
+        "bq256_bkv128_d64_bf16": (1, 2, 777, 64, 256, 128, "bf16", 24, 0.20, 0.50),
+        "bq64_bkv32_d64_bf16": (1, 2, 700, 64, 64, 32, "bf16", 25, 0.10, 0.40),
+        "bq64_bkv32_f32": (1, 2, 600, 64, 64, 32, "f32", 26, 0.15, 0.50),
+        "bq256_bkv128_f32": (1, 2, 600, 128, 256, 128, "f32", 27, 0.25, 0.50),
     }[name]
-    B, H, N, D, BQ, dt, seed, k, p = spec
-    return synth.sink_inputs(B, H, N, D, 64, seed=seed, dtype=dt), BQ, 64, k, p
+    B, H, N, D, BQ, BKV, dt, seed, k, p = spec
+    return synth.sink_inputs(B, H, N, D, 64, seed=seed, dtype=dt), BQ, BKV, k, p
 
 
 CASES = ["tiny_fp32", "ragged_bf16", "ragged_bf16_d64", "ragged_f32_d128",
-         "ragged_f32_d64_bq128", "single_block", "one_row", "mid_bf16"]
+         "ragged_f32_d64_bq128", "single_block", "one_row", "mid_bf16",
+         "bkv32_bf16", "bkv128_bf16", "bq256_bf16", "bq256_bkv128_d64_bf16",
+         "bq64_bkv32_d64_bf16", "bq64_bkv32_f32", "bq256_bkv128_f32"]
 _CACHE = {}
 
 
