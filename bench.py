@@ -144,6 +144,10 @@ def main():
                     help="only run a plain 512 MiB device copy (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="Top-k / Top-p / hybrid sweep on near-uniform and skewed rows")
+    ap.add_argument("--bq", type=int, default=None,
+                    help="query block size (64, 128, 256); p is recalibrated on the GPU to the "
+                         "workload's target kept fraction")
+    ap.add_argument("--bkv", type=int, default=None, help="key block size (32, 64, 128)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus "
@@ -173,6 +177,21 @@ def main():
 
     q, k, v = (_dev(getattr(inp, n)) for n in ("q", "k", "v"))
     do = _dev(inp.do) if train else None
+    calibrated = None
+    if (args.bq or bq) != bq or (args.bkv or bkv) != bkv:
+        # block-size variant: same inputs and k, p re-tuned to the same kept fraction
+        from block_sparse_attention_spa2_amd.calibrate import calibrate
+        target = configs.WORKLOADS[args.workload].get("target_kept")
+        if target is None:
+            sys.exit(f"--bq/--bkv need a workload with a target kept fraction; "
+                     f"{args.workload} has none")
+        bq, bkv = args.bq or bq, args.bkv or bkv
+        cal = calibrate(q, k, kf, target, bq, bkv)
+        pf = cal.p
+        w = dict(w, BQ=bq, BKV=bkv, p=pf)
+        calibrated = {"target_kept": target, "kept_pairs": cal.kept_pairs, "pairs": cal.pairs,
+                      "interval": list(cal.interval)}
+        log(f"[bench] block sizes {bq}/{bkv}: p calibrated to {pf} ({cal.kept_fraction:.6f} kept)")
     bm = spa2.BlockMask.empty(B, H, N, bq, bkv, q.device)
     mws = torch.empty(spa2.mask_workspace_size(q, bq, bkv), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
@@ -283,7 +302,7 @@ def main():
     roofline = dict(bound="mfma", kernel=dom, achieved=round(achieved, 2),
                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                    traffic=recorded_traffic(dom, args.workload),
+                    traffic=None if calibrated else recorded_traffic(dom, args.workload),
                     flops_per_launch=kernel_flops[dom], ms_per_launch=round(per_stage[dom], 4))
     mask_bytes = 2.0 * B * H * N * D * q.element_size()  # Q and K read once
     copy_gbs = copy_bandwidth()
@@ -292,7 +311,7 @@ def main():
     kernels = {}
     for name, fl in kernel_flops.items():
         t = per_stage[name] * 1e-3
-        rec = recorded_traffic(name, args.workload)
+        rec = None if calibrated else recorded_traffic(name, args.workload)  # recorded at 128/64
         kernels[name] = {"ms": round(per_stage[name], 4), "tflops": round(fl / t / 1e12, 2),
                          "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "traffic_bytes": rec,
@@ -330,7 +349,7 @@ def main():
         "data": f"synthetic (seeded generator, {shape} attention shape)",
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "D": D, "bq": bq,
                    "bkv": bkv, "k": kf, "p": pf, "kept_fraction": round(kept_frac, 6),
-                   "kept_area_tokens2": area,
+                   "kept_area_tokens2": area, "p_calibrated": calibrated,
                    "step": "mask+fwd+bwd" if train else "mask+fwd"},
         "roofline": roofline,
         "kernels": kernels,
