@@ -7,14 +7,17 @@
 //   dQ = dS K / sqrt(D),   dK = dS^T Q / sqrt(D),   dV = P^T dO,
 // summed over kept block pairs only. P is rebuilt from the forward's LSE.
 //
-// Three deterministic kernels:
-//   bwd_pre   Dv = rowsum(dO * O) (fp32), one pass over O and dO;
-//   bwd_dkdv  one workgroup per key block, looping over the query blocks that keep it
-//             (column lists); the four waves split the block 2 x 2 (key halves of 32
-//             x query halves), Q_i and dO_i are staged in LDS, and the two query
-//             halves' partial dK/dV are summed through LDS at the end;
-//   bwd_dq    one workgroup per query block, looping over its kept key blocks (row
-//             lists), like the forward; K_j and V_j are staged in LDS.
+// Deterministic kernels (spa2_bwd runs the dQ pass with the row term, then dK/dV):
+//   bwd_pre   Dv = rowsum(dO * O) (fp32), one pass over O and dO (the staged call only);
+//   bwd_dq    one workgroup per query tile, looping over its kept key tiles (row lists),
+//             like the forward; K_j and V_j are staged in LDS; optionally computes Dv of
+//             its rows first (the row term) and writes it for the dK/dV pass;
+//   bwd_dkdv  one workgroup per key tile, looping over the query tiles that keep it
+//             (column lists); the waves split the pair into key groups x query groups,
+//             Q_i and dO_i are staged in LDS, and the query groups' partial dK/dV are
+//             summed through LDS at the end.
+// Tiles are at most 128 query rows and 64 keys; a 256-row or 128-key mask block is two
+// consecutive tiles over the same list entry (TileQueue).
 #include <math.h>
 
 #include <type_traits>

@@ -6,11 +6,12 @@
 // accumulates P_ij V_j. Masked pairs are skipped entirely: their K/V tiles are never
 // fetched.
 //
-// One workgroup (4 waves) per query block; two workgroups share a CU (2 waves per SIMD,
-// so one wave's softmax overlaps the other's matrix work). Wave w owns BQ/4 query rows.
-// K_j and V_j (64 x D) stream from global memory straight into a double-buffered,
-// swizzled LDS tile (global_load_lds), issued one block ahead, with one barrier per
-// block. Scores are computed transposed, S^T = K Q^T (operand A = K rows from LDS,
+// One workgroup (4 waves) per query tile of 64 or 128 rows (a 256-row block is two
+// tiles); two workgroups share a CU (2 waves per SIMD, so one wave's softmax overlaps
+// the other's matrix work). Wave w owns a quarter of the tile's rows. Key tiles of 32 or
+// 64 rows (a 128-key block is two tiles) of K and V stream from global memory straight
+// into a double-buffered, swizzled LDS tile (global_load_lds), issued one tile ahead,
+// with one barrier per tile. Scores are computed transposed, S^T = K Q^T (operand A = K rows from LDS,
 // operand B = Q held in registers), so each lane owns one query column and the
 // online-softmax state is lane local (the row max needs the 4 lanes that share the
 // column, combined with VALU lane swaps). P^T leaves the accumulators directly as the
