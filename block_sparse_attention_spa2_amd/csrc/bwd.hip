@@ -215,6 +215,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   // last eight blocks (bf16, the newest in element 7): at the end of a batch of eight,
   // element i is block i of the batch.
   u32x4 wr[QT], wp[QT];
+  // the last block's sums, taken into the weights at the start of the next block (so the
+  // wait for the 0/1-operand MFMA is off the block's critical path)
+  float pend_tb[QT], pend_pb[QT];
+  f32x4 pend_cs[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     tpart[qt] = 0.f;
@@ -239,6 +243,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     const unsigned b = __builtin_bit_cast(unsigned short, (bf16)x);
     r = u32x4{__builtin_amdgcn_alignbit(r[1], r[0], 16), __builtin_amdgcn_alignbit(r[2], r[1], 16),
               __builtin_amdgcn_alignbit(r[3], r[2], 16), __builtin_amdgcn_alignbit(b, r[3], 16)};
+  };
+  auto take_pending = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      tpart[qt] += pend_tb[qt];
+      const float bsum = g == 0 ? pend_cs[qt][0] : g == 1 ? pend_cs[qt][1] : g == 2 ? pend_cs[qt][2] : pend_cs[qt][3];
+      shift_in(wr[qt], pend_tb[qt] - bsum);
+      shift_in(wp[qt], pend_pb[qt]);
+    }
   };
   // C rows: block i of a batch at rows 4 g' + i (i < 4) or 16 + 4 g' + (i - 4), g' = 0..3,
   // so that the transpose reads of every lane group see c_0 .. c_7 in slots 0..7
@@ -277,6 +290,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     if constexpr (kCorr) {
       // the previous batch's C rows are now visible to every wave; its weights are the
       // shift registers' contents (this block has not shifted in yet)
+      if (t > 0) take_pending();  // the previous block's weights
       if ((t & 7) == 0 && t > 0) flush(((t >> 3) & 1) ? cm0 : cm1);
       // this block's first key row, four copies (one per lane group)
       if (w == 0) {
@@ -359,12 +373,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     if constexpr (kCorr) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        tpart[qt] += tb[qt];
         // this group's share of sum_k r_k: its fp32 partial of sum_k dS_k minus its partial
-        // of sum_k bf16(dS_k) (small: bf16 keeps the weight's own rounding negligible)
-        const float bsum = g == 0 ? cs[qt][0] : g == 1 ? cs[qt][1] : g == 2 ? cs[qt][2] : cs[qt][3];
-        shift_in(wr[qt], tb[qt] - bsum);
-        shift_in(wp[qt], pb[qt]);
+        // of sum_k bf16(dS_k) (small: bf16 keeps the weight's own rounding negligible);
+        // taken into the weights at the start of the next block
+        pend_tb[qt] = tb[qt];
+        pend_pb[qt] = pb[qt];
+        pend_cs[qt] = cs[qt];
       }
     }
   };
@@ -383,6 +397,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 
   if constexpr (kCorr) {
     if (cnt > 0) {
+      take_pending();  // the last block's weights
       // complete the last batch with zero weights, then apply it
       const int last = cnt - 1;
       for (int t = last + 1; (t & 7) != 0; ++t)
