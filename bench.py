@@ -559,7 +559,20 @@ def cpu_baseline(inp, w, gmask, total_flops, budget_s=20.0):
                        f"every {stride}th query block of those heads ({qblocks_done} of "
                        f"{B * H * tm} blocks), extrapolated to the full step "
                        f"({est:.1f} s estimated)"),
-            "seconds_measured": round(time.time() - t_start, 1)}
+            "seconds_measured": round(time.time() - t_start, 1), "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 if __name__ == "__main__":
