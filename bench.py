@@ -312,6 +312,16 @@ def main():
                     flops_per_launch=kernel_flops[dom], ms_per_launch=round(per_stage[dom], 4))
     mask_bytes = 2.0 * B * H * N * D * q.element_size()  # Q and K read once
     copy_gbs = copy_bandwidth()
+    # the mask stage split: pooling (reads Q and K: the HBM-bound part) against the rest
+    # (fp64 P-bar GEMM, per-row selection, lists), from separate timed pool calls
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    spa2.pool(q, k, bq, bkv)
+    pe[0].record()
+    for _ in range(10):
+        spa2.pool(q, k, bq, bkv)
+    pe[1].record()
+    torch.cuda.synchronize()
+    pool_ms = pe[0].elapsed_time(pe[1]) / 10
     # every timed kernel against both ceilings: MFMA (algorithmic flops) and memory (the
     # recorded counter bytes, when the kernel is unchanged since they were taken)
     kernels = {}
@@ -368,6 +378,9 @@ def main():
         ("fwd_bwd_tflops" if train else "fwd_only_tflops"):
             round((flops_fwd + flops_bwd) / (sparse_attn * 1e-3) / 1e12, 2),
         "fwd_tflops": round(flops_fwd / (per_stage["fwd"] * 1e-3) / 1e12, 2),
+        "mask_split_ms": {"pool": round(pool_ms, 4),
+                          "scores_select_lists": round(per_stage["mask"] - pool_ms, 4),
+                          "pool_GB/s": round(mask_bytes / (pool_ms * 1e-3) / 1e9, 1)},
         "mask_hbm": {"bytes": mask_bytes,
                      "GB/s": round(mask_bytes / (per_stage["mask"] * 1e-3) / 1e9, 1),
                      "frac": round(mask_bytes / (per_stage["mask"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
