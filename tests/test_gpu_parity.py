@@ -153,7 +153,8 @@ def test_bwd(name):
     print(f"[{name}] bwd {out}")
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_f32_d64_bq128"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_f32_d64_bq128",
+                                  "bq256_bkv128_d64_bf16", "bq64_bkv32_d64_bf16"])
 def test_end_to_end_mask_fwd_bwd(name):
     """GPU mask -> GPU forward -> GPU backward, compared with the oracle's whole chain."""
     r = ref(name)
@@ -168,7 +169,8 @@ def test_end_to_end_mask_fwd_bwd(name):
         gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_bf16_d64"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_bf16_d64", "bkv32_bf16",
+                                  "bkv128_bf16", "bq256_bkv128_f32"])
 def test_dense_path(name):
     """mask = NULL runs every block; it equals the all-ones mask bit for bit and the
     oracle's dense attention."""
