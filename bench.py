@@ -532,17 +532,17 @@ def check_parity(inp, w, gmask, o, lse, dq, dk, dv):
             "seconds": round(time.time() - t0, 1)}
 
 
-def cpu_baseline(inp, w, gmask, total_flops, budget_s=20.0):
+def cpu_baseline(inp, w, gmask, total_flops, budget_s=20.0, stride=1):
     """The float64 oracle on a bounded sample of the workload, extrapolated to the whole
-    step: the mask of whole heads plus forward and backward of evenly spaced query
-    blocks, repeated head by head until about `budget_s` seconds have passed."""
+    step: the mask of whole heads plus forward and backward of every `stride`-th query
+    block, repeated head by head until about `budget_s` seconds have passed (at 480p the
+    whole step fits in that time)."""
     import numpy as np
 
     import oracle
 
     B, H, N, D, bq, bkv = w["B"], w["H"], w["N"], w["D"], w["BQ"], w["BKV"]
     tm = gmask.shape[2]
-    stride = 4
     t_mask = t_fb = 0.0
     heads = 0
     qblocks_done = 0
@@ -569,7 +569,8 @@ def cpu_baseline(inp, w, gmask, total_flops, budget_s=20.0):
             "cores": min(threads, len(os.sched_getaffinity(0))), "kind": "oracle",
             "sample": (f"float64 oracle: mask of {heads} whole head(s) and forward"
                        f"{'+backward' if inp.do is not None else ''} of "
-                       f"every {stride}th query block of those heads ({qblocks_done} of "
+                       f"{'every' if stride == 1 else f'every {stride}th'} query block of "
+                       f"those heads ({qblocks_done} of "
                        f"{B * H * tm} blocks), extrapolated to the full step "
                        f"({est:.1f} s estimated)"),
             "seconds_measured": round(time.time() - t_start, 1), "cpu_model": _cpu_model()}

@@ -54,9 +54,13 @@ spa2_status check_blockmask(const spa2_blockmask* m, bool need_lists) {
   return SPA2_OK;
 }
 
+// The mask workspace holds q-bar, k-bar (rows kPoolPitch(D) doubles apart) and the pooled
+// scores (double), from the first 256-byte boundary of the caller's buffer: the slack
+// makes any start address usable.
+constexpr size_t kWsAlign = 256;
 size_t mask_ws_bytes(const spa2::Shape& s) {
-  const size_t bh = (size_t)s.BH();
-  return bh * ((size_t)(s.Tm + s.Tn) * s.D + (size_t)s.Tm * s.Tn) * sizeof(double);
+  const size_t bh = (size_t)s.BH(), pitch = (size_t)spa2::kPoolPitch(s.D);
+  return bh * ((size_t)(s.Tm + s.Tn) * pitch + (size_t)s.Tm * s.Tn) * sizeof(double) + kWsAlign;
 }
 
 spa2_status hip_status(const char* where, hipError_t e) {
@@ -70,14 +74,11 @@ spa2_status hip_status(const char* where, hipError_t e) {
 // L2); key blocks go longest first across the whole part (a head's attention-sink column
 // can hold most of the query blocks and must start first).
 spa2_status write_orders(const spa2::Shape& s, const spa2_blockmask& m, hipStream_t hs) {
-  spa2_status st = SPA2_OK;
-  if (m.row_order &&
-      (st = hip_status("order", spa2::launch_order(m.row_cnt, s.BH() * s.Tm, s.Tn, s.Tm,
-                                                   m.row_order, hs))) != SPA2_OK)
-    return st;
-  if (m.col_order)
-    st = hip_status("order", spa2::launch_order(m.col_cnt, s.BH() * s.Tn, s.Tm, 0, m.col_order, hs));
-  return st;
+  // rows head by head (per_head = T_m), columns by count over the whole range
+  const spa2::OrderJob rows{m.row_cnt, s.BH() * s.Tm, s.Tn, s.Tm, m.row_order};
+  const spa2::OrderJob cols{m.col_cnt, s.BH() * s.Tn, s.Tm, 0, m.col_order};
+  return hip_status("order", spa2::launch_orders(m.row_order ? &rows : nullptr,
+                                                 m.col_order ? &cols : nullptr, hs));
 }
 
 }  // namespace
@@ -110,7 +111,7 @@ spa2_status spa2_pool(const spa2_desc* desc, const void* q, const void* k, doubl
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
   if (!q || !k || !qbar || !kbar) return SPA2_E_NULL;
-  return hip_status("pool", spa2::launch_pool(s, q, k, qbar, kbar, (hipStream_t)stream));
+  return hip_status("pool", spa2::launch_pool(s, q, k, qbar, kbar, s.D, (hipStream_t)stream));
 }
 
 spa2_status spa2_mask_workspace_size(const spa2_desc* desc, size_t* bytes) {
@@ -134,11 +135,12 @@ spa2_status spa2_mask(const spa2_desc* desc, const void* q, const void* k, doubl
   if (!workspace || ws_bytes < mask_ws_bytes(s)) return SPA2_E_WORKSPACE;
 
   const hipStream_t hs = (hipStream_t)stream;
-  double* qbar = (double*)workspace;
-  double* kbar = qbar + (size_t)s.BH() * s.Tm * s.D;
-  double* scores = kbar + (size_t)s.BH() * s.Tn * s.D;
-  if ((st = hip_status("pool", spa2::launch_pool(s, q, k, qbar, kbar, hs))) != SPA2_OK) return st;
-  if ((st = hip_status("scores", spa2::launch_scores(s, qbar, kbar, scores, hs))) != SPA2_OK)
+  double* qbar = (double*)(((uintptr_t)workspace + kWsAlign - 1) & ~(uintptr_t)(kWsAlign - 1));
+  const int pitch = spa2::kPoolPitch(s.D);
+  double* kbar = qbar + (size_t)s.BH() * s.Tm * pitch;
+  double* scores = kbar + (size_t)s.BH() * s.Tn * pitch;
+  if ((st = hip_status("pool", spa2::launch_pool(s, q, k, qbar, kbar, pitch, hs))) != SPA2_OK) return st;
+  if ((st = hip_status("scores", spa2::launch_scores(s, qbar, kbar, pitch, scores, hs))) != SPA2_OK)
     return st;
   if ((st = hip_status("select", spa2::launch_select(s, scores, true, pbar_out,
                                                      topk_count(k_frac, s.Tn), p_frac, *out,

@@ -24,15 +24,28 @@ struct Shape {
 // per lane at most.
 constexpr int kMaxTn = 4096;
 
+// q-bar / k-bar rows are `pitch` doubles apart (D for the public layout; the mask
+// workspace uses kPoolPitch(D))
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar,
-                       hipStream_t st);
-hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar, double* scores,
-                         hipStream_t st);
+                       int pitch, hipStream_t st);
+hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar, int pitch,
+                         double* scores, hipStream_t st);
+constexpr int kPoolPitch(int D) { return D + 2; }
 // from_scores: src holds raw pooled scores (softmax applied here); else src holds P-bar.
 hipError_t launch_select(const Shape& s, const double* src, bool from_scores, double* pbar_out,
                          int n_k, double p_frac, const spa2_blockmask& m, hipStream_t st);
-hipError_t launch_order(const int32_t* cnt, int items, int maxc, int per_head, int32_t* order,
-                        hipStream_t st);
+// A scheduling order to list: the kept counts of `items` lists (clamped to [0, maxc]),
+// written as a permutation to `order`; per_head > 0 groups the items head by head
+// (per_head items per head), 0 sorts the whole range by count.
+struct OrderJob {
+  const int32_t* cnt;
+  int items;
+  int maxc;
+  int per_head;
+  int32_t* order;
+};
+// One launch for up to two orders (either pointer may be NULL).
+hipError_t launch_orders(const OrderJob* a, const OrderJob* b, hipStream_t st);
 hipError_t launch_rows(const Shape& s, const spa2_blockmask& m, hipStream_t st);
 hipError_t launch_cols(const Shape& s, const spa2_blockmask& m, hipStream_t st);
 

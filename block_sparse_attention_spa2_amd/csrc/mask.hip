@@ -27,7 +27,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    double* __restrict__ qbar,
                                                    double* __restrict__ kbar, int BH, int N, int BQ,
-                                                   int BKV, int Tm, int Tn) {
+                                                   int BKV, int Tm, int Tn, int pitch) {
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int TPR = D / EPC;              // threads per row
   constexpr int RP = 256 / TPR;             // rows in flight
@@ -69,63 +69,75 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   if (threadIdx.x < D) {
     double s = 0.0;
     for (int r = 0; r < RP; ++r) s += red[r][threadIdx.x];
-    dst[((size_t)bh * nblk + blk) * D + threadIdx.x] = s / (double)(hi - lo);
+    dst[((size_t)bh * nblk + blk) * pitch + threadIdx.x] = s / (double)(hi - lo);
   }
 }
 
 // ------------------------------------------------------------------------------------
 // Pooled scores S-bar = q-bar k-bar^T / sqrt(D) on the fp64 matrix cores
-// (v_mfma_f64_16x16x4_f64). Workgroup tile 64 x 64; wave w owns rows [16w, 16w+16).
+// (v_mfma_f64_16x16x4_f64). One wave per 16 x 32 output tile (two 16 x 16 MFMA tiles),
+// four consecutive tiles per workgroup, operands loaded straight into registers, no LDS
+// and no barrier. Lane (g, c) = (l / 16, l % 16) loads dims 8 i + 2 g and 8 i + 2 g + 1
+// of row c (A: query block, B: key block) with one 16-byte load, so the four lane groups
+// of a row read 64 contiguous bytes per load; those two dims feed reduction slot g at
+// steps 2 i and 2 i + 1. The dot product is the same sum in any slot order. Rows and keys
+// past the matrix read a clamped row and are not stored. `pitch` (doubles) is the row
+// stride of q-bar and k-bar: with rows exactly 1 KB apart the sixteen rows of one load
+// meet in a few L2 channels, and a pitch of D + 2 spreads them (measured: the operand
+// loads take 14 instead of 22 us at 12 x 256 x 512 blocks).
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qbar,
                                                      const double* __restrict__ kbar,
                                                      double* __restrict__ scores, int Tm, int Tn,
-                                                     int tiles_m, int tiles_n, double sqrt_d) {
-  constexpr int KC = 32;       // reduction chunk
-  constexpr int PITCH = KC + 1;  // doubles; odd pitch spreads rows over banks
-  __shared__ double qs[64 * PITCH];
-  __shared__ double ks[64 * PITCH];
-
+                                                     int pitch, int tiles_m, int tiles_n, int tiles,
+                                                     double sqrt_d) {
+  constexpr int NS = D / 4;  // MFMA steps (four dims each)
+  // XCD-contiguous workgroup order: an XCD covers a range of heads, whose pooled vectors
+  // then stay in its L2 for every tile that reads them
+  const int tile = xcd_item(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+  if (tile >= tiles) return;  // whole wave leaves; no barrier below
+  const int l = lane_id(), g = l >> 4, c16 = l & 15;
   const int per_head = tiles_m * tiles_n;
-  const int bh = blockIdx.x / per_head;
-  const int tm = (blockIdx.x % per_head) / tiles_n, tn = blockIdx.x % tiles_n;
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, g = l >> 4, c16 = l & 15;
-  const double* qb = qbar + (size_t)bh * Tm * D;
-  const double* kb = kbar + (size_t)bh * Tn * D;
+  const int bh = tile / per_head;
+  const int tm = (tile % per_head) / tiles_n, tn = tile % tiles_n;
 
-  f64x4 acc[4];
+  const double* qrow = qbar + ((size_t)bh * Tm + min(tm * 16 + c16, Tm - 1)) * pitch + 2 * g;
+  double a[NS], b[2][NS];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
-
-  for (int dc = 0; dc < D; dc += KC) {
-    for (int e = threadIdx.x; e < 64 * KC; e += 256) {
-      const int r = e / KC, cc = e % KC;
-      const int qi = tm * 64 + r, kj = tn * 64 + r;
-      qs[r * PITCH + cc] = qi < Tm ? qb[(size_t)qi * D + dc + cc] : 0.0;
-      ks[r * PITCH + cc] = kj < Tn ? kb[(size_t)kj * D + dc + cc] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k4 = 0; k4 < KC; k4 += 4) {
-      const double a = qs[(w * 16 + c16) * PITCH + k4 + g];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const double bv = ks[(ct * 16 + c16) * PITCH + k4 + g];
-        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[ct], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < NS / 2; ++i) {
+    const f64x2 x = *reinterpret_cast<const f64x2*>(qrow + 8 * i);
+    a[2 * i] = x[0];
+    a[2 * i + 1] = x[1];
   }
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const double* krow = kbar + ((size_t)bh * Tn + min(tn * 32 + ct * 16 + c16, Tn - 1)) * pitch + 2 * g;
+#pragma unroll
+    for (int i = 0; i < NS / 2; ++i) {
+      const f64x2 x = *reinterpret_cast<const f64x2*>(krow + 8 * i);
+      b[ct][2 * i] = x[0];
+      b[ct][2 * i + 1] = x[1];
+    }
+  }
+  // every load is in flight before the first product (one memory round trip per wave)
+  __builtin_amdgcn_sched_barrier(0);
+  f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[ct][i], acc[ct], 0, 0, 0);
+
   // v_mfma_f64_16x16x4_f64 returns C[g + 4 e][l % 16] in element e of lane l (the fp32
   // results use 4 g + e instead).
   double* out = scores + (size_t)bh * Tm * Tn;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int col = tn * 64 + ct * 16 + c16;
+  for (int ct = 0; ct < 2; ++ct) {
+    const int col = tn * 32 + ct * 16 + c16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = tm * 64 + w * 16 + g + 4 * e;
+      const int row = tm * 16 + g + 4 * e;
       if (row < Tm && col < Tn) out[(size_t)row * Tn + col] = acc[ct][e] / sqrt_d;
     }
   }
@@ -179,6 +191,29 @@ __device__ __forceinline__ int wave_min_int(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
   return x;
+}
+// Ordering key of a window head: the high word of a positive double (sign, exponent
+// and the top 20 mantissa bits, which order like the value), 0 for the empty slot (-1).
+__device__ __forceinline__ unsigned key_hi(double x) {
+  return x > 0.0 ? (unsigned)(__builtin_bit_cast(unsigned long long, x) >> 32) : 0u;
+}
+__device__ __forceinline__ unsigned max_dpp_u32_step(unsigned x, unsigned y) { return x > y ? x : y; }
+__device__ __forceinline__ unsigned wave_max_u32(unsigned x) {
+  x = max_dpp_u32_step(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
+  x = max_dpp_u32_step(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
+  x = max_dpp_u32_step(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
+  x = max_dpp_u32_step(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max_dpp_u32_step((unsigned)r16[0], (unsigned)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max_dpp_u32_step((unsigned)r32[0], (unsigned)r32[1]);
+}
+// A double from lane `src` (wave-uniform) to every lane.
+__device__ __forceinline__ double readlane_f64(double x, int src) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, src);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), src);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
 // ------------------------------------------------------------------------------------
@@ -274,18 +309,34 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   };
   refill(2.0, -1);  // every block (all values are below 2)
 
-  // 3. ranks in order until the first rejected one
+  // 3. ranks in order until the first rejected one. The wave maximum is taken first on
+  // the high 32 bits of the window heads (positive doubles order like their bit patterns,
+  // so one DPP max per step); if a single lane holds that maximum it owns the rank.
+  // Otherwise (equal high words, or nothing positive left) the double maximum and the
+  // index rule for equal values decide.
   unsigned long long kept = 0;  // bit t: block l + 64 t is kept
   double prefix = 0.0;          // e_r, summed in rank order
   int rank = 0;
+  unsigned key = key_hi(wv[0]);
+  // rank, prefix, m and owner are wave-uniform (read from one lane), so the loop and its
+  // exits are scalar control flow
   for (;;) {
-    const double m = wave_max_fast(wv[0]);
-    if (m < 0.0) break;                              // every block is kept
-    if (rank >= n_k && !(prefix < p_frac)) break;    // rank r fails both tests
-    const unsigned long long tie = __builtin_amdgcn_ballot_w64(wv[0] == m);
-    int owner = __builtin_ctzll(tie);
-    if ((tie & (tie - 1)) != 0)  // equal values in several lanes: smallest block index
-      owner = wave_min_int(wv[0] == m ? l + 64 * wt[0] : INT_MAX) & 63;
+    if (rank >= n_k && !(prefix < p_frac)) break;  // rank r fails both tests
+    const unsigned mk = __builtin_amdgcn_readfirstlane(wave_max_u32(key));
+    const unsigned long long cand = __builtin_amdgcn_ballot_w64(key == mk);
+    double m;
+    int owner;
+    if (mk != 0u && (cand & (cand - 1)) == 0) {
+      owner = __builtin_ctzll(cand);
+      m = readlane_f64(wv[0], owner);
+    } else {
+      m = readlane_f64(wave_max_fast(wv[0]), 0);
+      if (m < 0.0) break;  // every block is kept
+      const unsigned long long tie = __builtin_amdgcn_ballot_w64(wv[0] == m);
+      owner = __builtin_ctzll(tie);
+      if ((tie & (tie - 1)) != 0)  // equal values in several lanes: smallest block index
+        owner = __builtin_amdgcn_readfirstlane(wave_min_int(wv[0] == m ? l + 64 * wt[0] : INT_MAX)) & 63;
+    }
     if (l == owner) {
       const int lt = wt[0];
       kept |= 1ull << lt;
@@ -296,6 +347,7 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
       }
       wv[W - 1] = -1.0;
       if (wv[0] < 0.0) refill(m, lt);
+      key = key_hi(wv[0]);
     }
     prefix += m;
     ++rank;
@@ -351,6 +403,7 @@ __global__ __launch_bounds__(256) void cols_kernel(const uint8_t* __restrict__ m
   const uint8_t* m = mask + (size_t)bh * Tm * Tn;
   int n = 0;
   if (j < Tn)
+#pragma unroll 8
     for (int i = i0; i < i1; ++i) n += m[(size_t)i * Tn + j];
   cnts[part][c] = n;
   __syncthreads();
@@ -358,6 +411,7 @@ __global__ __launch_bounds__(256) void cols_kernel(const uint8_t* __restrict__ m
   for (int p = 0; p < part; ++p) off += cnts[p][c];
   if (j < Tn) {
     int32_t* out = col_idx + ((size_t)bh * Tn + j) * Tm;
+#pragma unroll 8
     for (int i = i0; i < i1; ++i)
       if (m[(size_t)i * Tn + j]) out[off++] = i;
     if (part == 15) col_cnt[(size_t)bh * Tn + j] = off;
@@ -368,11 +422,11 @@ __global__ __launch_bounds__(256) void cols_kernel(const uint8_t* __restrict__ m
 // Launchers
 // ------------------------------------------------------------------------------------
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qbar, double* kbar,
-                       hipStream_t st) {
+                       int pitch, hipStream_t st) {
   const dim3 grid(s.BH() * (s.Tm + s.Tn));
 #define SPA2_POOL(T, D)                                                                      \
   pool_kernel<T, D><<<grid, 256, 0, st>>>((const T*)q, (const T*)k, qbar, kbar, s.BH(), s.N, \
-                                          s.BQ, s.BKV, s.Tm, s.Tn)
+                                          s.BQ, s.BKV, s.Tm, s.Tn, pitch)
   if (s.dtype == SPA2_BF16) {
     if (s.D == 64) SPA2_POOL(bf16, 64); else SPA2_POOL(bf16, 128);
   } else {
@@ -382,15 +436,16 @@ hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qba
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar, double* scores,
-                         hipStream_t st) {
-  const int tm = (s.Tm + 63) / 64, tn = (s.Tn + 63) / 64;
-  const dim3 grid(s.BH() * tm * tn);
+hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar, int pitch,
+                         double* scores, hipStream_t st) {
+  const int tm = (s.Tm + 15) / 16, tn = (s.Tn + 31) / 32;
+  const int tiles = s.BH() * tm * tn;  // one wave each, four per workgroup
+  const dim3 grid((tiles + 3) / 4);
   const double sqrt_d = sqrt((double)s.D);
   if (s.D == 64)
-    scores_kernel<64><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, tm, tn, sqrt_d);
+    scores_kernel<64><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, pitch, tm, tn, tiles, sqrt_d);
   else
-    scores_kernel<128><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, tm, tn, sqrt_d);
+    scores_kernel<128><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, pitch, tm, tn, tiles, sqrt_d);
   return hipGetLastError();
 }
 
@@ -423,14 +478,17 @@ hipError_t launch_select(const Shape& s, const double* src, bool from_scores, do
 // same time on one XCD mostly read one head's tiles (more L2 reuse); if the part spans too
 // many heads for the histogram, the plain order is used. Items with equal keys land in the
 // order of their atomic increments.
-__global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ cnt, int items,
-                                                    int maxc, int per_head,
-                                                    int32_t* __restrict__ order) {
+__global__ __launch_bounds__(256) void order_kernel(OrderJob j0, OrderJob j1) {
   constexpr int kBins = 16384;
   static_assert(kBins >= kMaxTn + 1, "the plain order always fits");
   __shared__ int hist[kBins];
   __shared__ int wsum[4];
-  const int tid = threadIdx.x, x = blockIdx.x;
+  // workgroups 0-7 list the parts of the first job, 8-15 those of the second
+  const OrderJob& job = blockIdx.x < 8 ? j0 : j1;
+  const int32_t* __restrict__ cnt = job.cnt;
+  int32_t* __restrict__ order = job.order;
+  const int items = job.items, maxc = job.maxc, per_head = job.per_head;
+  const int tid = threadIdx.x, x = blockIdx.x & 7;
   const int q = items >> 3, r = items & 7;
   const int lo = x * q + min(x, r), n = q + (x < r ? 1 : 0);
   const int nb = maxc + 1;
@@ -476,9 +534,10 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* __restrict__ 
   for (int i = tid; i < n; i += 256) order[lo + atomicAdd(&hist[bin(i)], 1)] = lo + i;
 }
 
-hipError_t launch_order(const int32_t* cnt, int items, int maxc, int per_head, int32_t* order,
-                        hipStream_t st) {
-  order_kernel<<<8, 256, 0, st>>>(cnt, items, maxc, per_head, order);
+hipError_t launch_orders(const OrderJob* a, const OrderJob* b, hipStream_t st) {
+  if (!a && !b) return hipSuccess;
+  if (a && b) order_kernel<<<16, 256, 0, st>>>(*a, *b);
+  else order_kernel<<<8, 256, 0, st>>>(a ? *a : *b, a ? *a : *b);
   return hipGetLastError();
 }
 

@@ -104,8 +104,9 @@ int32_t spa2_num_blocks(int32_t n, int32_t block);
 spa2_status spa2_pool(const spa2_desc* desc, const void* q, const void* k, double* qbar,
                       double* kbar, void* stream);
 
-/* Workspace bytes that spa2_mask needs for this descriptor (pooled vectors and the
- * pooled score matrix, all double). */
+/* Workspace bytes that spa2_mask needs for this descriptor (pooled vectors, rows padded
+ * to D + 2, and the pooled score matrix, all double, plus 256 bytes so that the buffer
+ * may start at any address). */
 spa2_status spa2_mask_workspace_size(const spa2_desc* desc, size_t* bytes);
 
 /* Steps 1-3: pool, P-bar, Top-k U Top-p, compacted row and column lists.
