@@ -129,6 +129,52 @@ def test_select_on_oracle_pbar(name):
     assert cls["other"] == 0 and cls["k_band"] == 0, cls
 
 
+def _crafted_pbar_rows(tn, n_rows, seed):
+    """P-bar rows that drive every branch of the selection kernel: all values equal, two
+    levels, equal high 32 bits with different low bits, exact zeros, equal values in one
+    lane (blocks j and j + 64 share a lane) and in neighbouring lanes, and random rows."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    while len(rows) < n_rows:
+        cands = [
+            np.full(tn, 1.0),
+            np.where(rng.random(tn) < 0.2, 3.0, 1.0),
+            1.0 + rng.integers(0, 8, tn) * 2.0 ** -40,
+            np.where(rng.random(tn) < 0.05, rng.random(tn) + 0.1, 0.0),
+            np.resize(rng.random(64), tn),
+            np.repeat(rng.random((tn + 1) // 2), 2)[:tn],
+            np.r_[20.0, np.full(tn - 1, 1.0)],
+            # the pages' sink row when tn = 10 (its elided tail spread evenly)
+            np.r_[0.6, 0.2, 0.1, np.full(7, 0.1 / 7)] if tn == 10 else rng.random(tn),
+            rng.random(tn) ** 4,
+        ]
+        for c in cands:
+            if c.sum() == 0:
+                c[rng.integers(tn)] = 1.0
+            rows.append(c / c.sum())
+    return np.stack(rows[:n_rows])
+
+
+@pytest.mark.parametrize("n,seed", [(640, 0), (32768, 1), (5000, 2)])
+@pytest.mark.parametrize("kf,pf", [(0.2, 0.6), (0.02, 0.3), (0.1, 0.0), (0.0, 0.6), (0.5, 0.9)])
+def test_select_crafted_rows(n, seed, kf, pf):
+    """The selection kernel on crafted P-bar rows (ties, equal high words, zeros) keeps
+    exactly the oracle's blocks: both sides see the same values and sum the prefix in the
+    same rank order, so no band is excused. N = 640 gives the pages' 10-block rows."""
+    bq, bkv = 128, 64
+    tm, tn = spa2.num_blocks(n, bq), spa2.num_blocks(n, bkv)
+    pb = _crafted_pbar_rows(tn, tm, seed).reshape(1, 1, tm, tn)
+    like = torch.empty((1, 1, n, 64), dtype=torch.bfloat16, device="cuda")
+    bm = spa2.select(torch.from_numpy(pb).cuda(), kf, pf, like, bq, bkv)
+    got = bm.mask.cpu().numpy().astype(bool)[0, 0]
+    cnt = bm.row_cnt.cpu().numpy()[0, 0]
+    idx = bm.row_idx.cpu().numpy()[0, 0]
+    for i in range(tm):
+        want = oracle.select_row(pb[0, 0, i], kf, pf)["kept"]
+        assert list(np.flatnonzero(got[i])) == list(want), (i, kf, pf)
+        assert list(idx[i, :cnt[i]]) == list(want), (i, kf, pf)
+
+
 @pytest.mark.parametrize("name", CASES)
 def test_fwd(name):
     r = ref(name)

@@ -19,12 +19,18 @@ from gen import synth
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+def _ratio(text):
+    """A fixture entry written as a quotient, e.g. "0.1/7"."""
+    num, den = text.split("/")
+    return float(num) / float(den)
+
+
 def _rows():
     with open(os.path.join(GOLDEN, "worked_rows.json")) as f:
         g = json.load(f)
     rows = {}
     for name, vals in g["rows"].items():
-        rows[name] = np.array([eval(v) if isinstance(v, str) else v for v in vals])  # "0.1/7"
+        rows[name] = np.array([_ratio(v) if isinstance(v, str) else v for v in vals])
     return g, rows
 
 
