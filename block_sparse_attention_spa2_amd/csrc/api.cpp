@@ -27,9 +27,12 @@ spa2_status check_desc(const spa2_desc* d, spa2::Shape* out) {
   if (d->D != 64 && d->D != 128) return SPA2_E_SHAPE;
   if (d->BQ != 64 && d->BQ != 128 && d->BQ != 256) return SPA2_E_SHAPE;
   if (d->BKV != 32 && d->BKV != 64 && d->BKV != 128) return SPA2_E_SHAPE;
-  const int tn = blocks(d->N, d->BKV);
+  const int tn = blocks(d->N, d->BKV), tm = blocks(d->N, d->BQ);
   if (tn > spa2::kMaxTn) return SPA2_E_SHAPE;
-  *out = spa2::Shape{d->B, d->H, d->N, d->D, d->BQ, d->BKV, d->dtype, blocks(d->N, d->BQ), tn};
+  // launch grids are counted in int (up to two tiles per block): B*H*max(T_m, T_n) <= 2^26
+  // keeps them far from overflow and is beyond any problem that fits in device memory
+  if ((long long)d->B * d->H * (tm > tn ? tm : tn) > (1LL << 26)) return SPA2_E_SHAPE;
+  *out = spa2::Shape{d->B, d->H, d->N, d->D, d->BQ, d->BKV, d->dtype, tm, tn};
   return SPA2_OK;
 }
 

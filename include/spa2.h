@@ -25,7 +25,8 @@
  *     code and writes nothing. A failed kernel launch returns SPA2_E_HIP (details from
  *     spa2_last_error()). No C++ exception crosses this boundary.
  *   - Supported: dtype F32 or BF16, D in {64, 128}, BQ in {64, 128, 256},
- *     BKV in {32, 64, 128}, 1 <= N <= 2^20, B*H >= 1, T_n <= 4096. The method's sizes
+ *     BKV in {32, 64, 128}, 1 <= N <= 2^20, B*H >= 1, T_n <= 4096,
+ *     B*H*max(T_m, T_n) <= 2^26. The method's sizes
  *     are BQ = 128, BKV = 64; the others are the block-size variants the pages suggest
  *     trying (rainbus summary, "局限与改进": fixed block sizes are a limitation). The
  *     attention kernels work on tiles of at most 128 rows and 64 keys, so a 256-row or

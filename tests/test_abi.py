@@ -65,6 +65,7 @@ def test_status_strings():
     (dict(BQ=32), _lib.E_SHAPE), (dict(BQ=512), _lib.E_SHAPE), (dict(BQ=96), _lib.E_SHAPE),
     (dict(BKV=16), _lib.E_SHAPE), (dict(BKV=256), _lib.E_SHAPE), (dict(BKV=48), _lib.E_SHAPE),
     (dict(N=4096 * 64 + 1), _lib.E_SHAPE), (dict(N=4096 * 32 + 1, BKV=32), _lib.E_SHAPE),
+    (dict(B=1 << 12, H=1 << 12, N=4096), _lib.E_SHAPE),  # B*H*T_m past the grid bound
     (dict(dtype=7), _lib.E_DTYPE),
 ])
 def test_bad_desc(kw, code):
