@@ -7,7 +7,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libspa2.so")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_PARAM, E_WORKSPACE, E_HIP = range(7)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_PARAM, E_WORKSPACE, E_HIP, E_ALIGN = range(8)
 F32, BF16 = 0, 1
 
 

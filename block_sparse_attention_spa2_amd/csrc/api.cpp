@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "../../include/spa2.h"
 #include "kernels.h"
@@ -57,6 +58,23 @@ spa2_status check_blockmask(const spa2_blockmask* m, bool need_lists) {
   return SPA2_OK;
 }
 
+// Alignment the kernels' vector loads need: 16 bytes for [B, H, N, D] tensors (rows are
+// moved in 16-byte pieces), 8 for double arrays, 4 for float and int32 arrays. NULL passes.
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return false;
+  return true;
+}
+bool aligned4(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned(p, 4)) return false;
+  return true;
+}
+bool lists_aligned(const spa2_blockmask* m) {
+  return !m || aligned4({m->row_cnt, m->row_idx, m->col_cnt, m->col_idx, m->row_order, m->col_order});
+}
+
 // The mask workspace holds q-bar, k-bar (rows kPoolPitch(D) doubles apart) and the pooled
 // scores (double), from the first 256-byte boundary of the caller's buffer: the slack
 // makes any start address usable.
@@ -97,6 +115,7 @@ const char* spa2_status_str(spa2_status s) {
     case SPA2_E_PARAM: return "k/p fraction outside [0, 1], NaN, or both zero";
     case SPA2_E_WORKSPACE: return "workspace missing or too small";
     case SPA2_E_HIP: return "HIP runtime error";
+    case SPA2_E_ALIGN: return "a device pointer is not aligned for the kernels' vector loads";
   }
   return "unknown status";
 }
@@ -114,6 +133,7 @@ spa2_status spa2_pool(const spa2_desc* desc, const void* q, const void* k, doubl
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
   if (!q || !k || !qbar || !kbar) return SPA2_E_NULL;
+  if (!aligned16({q, k}) || !aligned(qbar, 8) || !aligned(kbar, 8)) return SPA2_E_ALIGN;
   return hip_status("pool", spa2::launch_pool(s, q, k, qbar, kbar, s.D, (hipStream_t)stream));
 }
 
@@ -136,6 +156,7 @@ spa2_status spa2_mask(const spa2_desc* desc, const void* q, const void* k, doubl
   if ((st = check_blockmask(out, true)) != SPA2_OK) return st;
   if ((st = check_fracs(k_frac, p_frac)) != SPA2_OK) return st;
   if (!workspace || ws_bytes < mask_ws_bytes(s)) return SPA2_E_WORKSPACE;
+  if (!aligned16({q, k}) || !aligned(pbar_out, 8) || !lists_aligned(out)) return SPA2_E_ALIGN;
 
   const hipStream_t hs = (hipStream_t)stream;
   double* qbar = (double*)(((uintptr_t)workspace + kWsAlign - 1) & ~(uintptr_t)(kWsAlign - 1));
@@ -161,6 +182,7 @@ spa2_status spa2_select(const spa2_desc* desc, const double* pbar, double k_frac
   if (!pbar) return SPA2_E_NULL;
   if ((st = check_blockmask(out, true)) != SPA2_OK) return st;
   if ((st = check_fracs(k_frac, p_frac)) != SPA2_OK) return st;
+  if (!aligned(pbar, 8) || !lists_aligned(out)) return SPA2_E_ALIGN;
   const hipStream_t hs = (hipStream_t)stream;
   if ((st = hip_status("select", spa2::launch_select(s, pbar, false, nullptr,
                                                      topk_count(k_frac, s.Tn), p_frac, *out,
@@ -175,6 +197,7 @@ spa2_status spa2_mask_lists(const spa2_desc* desc, const spa2_blockmask* m, void
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
   if ((st = check_blockmask(m, true)) != SPA2_OK) return st;
+  if (!lists_aligned(m)) return SPA2_E_ALIGN;
   const hipStream_t hs = (hipStream_t)stream;
   if ((st = hip_status("rows", spa2::launch_rows(s, *m, hs))) != SPA2_OK) return st;
   if ((st = hip_status("cols", spa2::launch_cols(s, *m, hs))) != SPA2_OK) return st;
@@ -189,6 +212,7 @@ spa2_status spa2_fwd(const spa2_desc* desc, const void* q, const void* k, const 
   if (st != SPA2_OK) return st;
   if (!q || !k || !v || !o || !lse) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
+  if (!aligned16({q, k, v, o, o_f32}) || !aligned(lse, 4) || !lists_aligned(m)) return SPA2_E_ALIGN;
   return hip_status("fwd", spa2::launch_fwd(s, q, k, v, m ? m->row_cnt : nullptr,
                                             m ? m->row_idx : nullptr, m ? m->row_order : nullptr,
                                             o, lse, o_f32, (hipStream_t)stream));
@@ -213,6 +237,9 @@ spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const 
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
   if (!workspace || ws_bytes < (size_t)s.BH() * s.N * sizeof(float)) return SPA2_E_WORKSPACE;
+  if (!aligned16({q, k, v, o, o_f32, dout, dq, dk, dv}) || !aligned4({lse, workspace}) ||
+      !lists_aligned(m))
+    return SPA2_E_ALIGN;
   return hip_status("bwd", spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, dk, dv,
                                             (float*)workspace, spa2::kBwdDqRow | spa2::kBwdDkdv,
                                             (hipStream_t)stream));
@@ -227,6 +254,8 @@ spa2_status spa2_bwd_dq_rowterm(const spa2_desc* desc, const void* q, const void
   if (st != SPA2_OK) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dvec || !dq) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
+  if (!aligned16({q, k, v, o, o_f32, dout, dq}) || !aligned4({lse, dvec}) || !lists_aligned(m))
+    return SPA2_E_ALIGN;
   return hip_status("bwd_dq_rowterm",
                     spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, nullptr, nullptr,
                                      dvec, spa2::kBwdDqRow, (hipStream_t)stream));
@@ -239,6 +268,9 @@ spa2_status spa2_error_terms(const spa2_desc* desc, const float* o_sparse, const
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
   if (!o_sparse || !lse_sparse || !o_dense || !lse_dense || !terms) return SPA2_E_NULL;
+  if (!aligned16({o_sparse, o_dense}) || !aligned4({lse_sparse, lse_dense, tau}) ||
+      !aligned(terms, 8))
+    return SPA2_E_ALIGN;
   return hip_status("error_terms",
                     spa2::launch_error_terms(s, o_sparse, lse_sparse, o_dense, lse_dense, terms,
                                              tau, (hipStream_t)stream));
@@ -250,6 +282,7 @@ spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
   if (!o || !dout || !dvec) return SPA2_E_NULL;
+  if (!aligned16({o, o_f32, dout}) || !aligned(dvec, 4)) return SPA2_E_ALIGN;
   return hip_status("bwd_prep", spa2::launch_bwd(s, nullptr, nullptr, nullptr, o, o_f32, nullptr, dout,
                                                  nullptr, nullptr, nullptr, nullptr, dvec,
                                                  spa2::kBwdPrep, (hipStream_t)stream));
@@ -263,6 +296,8 @@ spa2_status spa2_bwd_dkdv(const spa2_desc* desc, const void* q, const void* k, c
   if (st != SPA2_OK) return st;
   if (!q || !k || !v || !lse || !dout || !dvec || !dk || !dv) return SPA2_E_NULL;
   if (m && (!m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
+  if (!aligned16({q, k, v, dout, dk, dv}) || !aligned4({lse, dvec}) || !lists_aligned(m))
+    return SPA2_E_ALIGN;
   return hip_status("bwd_dkdv", spa2::launch_bwd(s, q, k, v, nullptr, nullptr, lse, dout, m, nullptr, dk,
                                                  dv, (float*)dvec, spa2::kBwdDkdv,
                                                  (hipStream_t)stream));
@@ -276,6 +311,8 @@ spa2_status spa2_bwd_dq(const spa2_desc* desc, const void* q, const void* k, con
   if (st != SPA2_OK) return st;
   if (!q || !k || !v || !lse || !dout || !dvec || !dq) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
+  if (!aligned16({q, k, v, dout, dq}) || !aligned4({lse, dvec}) || !lists_aligned(m))
+    return SPA2_E_ALIGN;
   return hip_status("bwd_dq", spa2::launch_bwd(s, q, k, v, nullptr, nullptr, lse, dout, m, dq, nullptr,
                                                nullptr, (float*)dvec, spa2::kBwdDq,
                                                (hipStream_t)stream));

@@ -16,6 +16,10 @@
  * Conventions shared by every call:
  *   - Tensor pointers are DEVICE pointers owned by the caller. Q, K, V, O, dO, dQ, dK, dV
  *     are contiguous [B, H, N, D] in desc->dtype (D fastest). LSE is float [B, H, N].
+ *   - Alignment (the kernels move rows in 16-byte pieces): [B, H, N, D] tensors and the
+ *     optional fp32 O start on a 16-byte boundary, double arrays on 8 bytes, float and
+ *     int32 arrays (LSE, Dv, lists, orders, workspaces other than the mask workspace) on
+ *     4 bytes. Every hipMalloc or PyTorch allocation is; otherwise SPA2_E_ALIGN.
  *   - Descriptor structs are HOST memory and are read during the call only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
  *     enqueues its kernels on that stream and returns without synchronising.
@@ -53,7 +57,8 @@ typedef enum {
   SPA2_E_DTYPE = 3,     /* unknown dtype */
   SPA2_E_PARAM = 4,     /* k or p outside [0, 1], NaN, or both zero */
   SPA2_E_WORKSPACE = 5, /* workspace NULL or smaller than the size call reports */
-  SPA2_E_HIP = 6        /* a HIP runtime call or kernel launch failed */
+  SPA2_E_HIP = 6,       /* a HIP runtime call or kernel launch failed */
+  SPA2_E_ALIGN = 7      /* a device pointer is not aligned as the conventions require */
 } spa2_status;
 
 typedef enum { SPA2_F32 = 0, SPA2_BF16 = 1 } spa2_dtype;

@@ -53,8 +53,9 @@ def mask_call(desc=None, q=FAKE, k=FAKE, kf=0.1, pf=0.5, out=None, ws=FAKE, wsb=
 
 def test_status_strings():
     L = _lib.lib()
-    for s in range(7):
-        assert L.spa2_status_str(s)
+    for s in range(8):
+        assert L.spa2_status_str(s) != b"unknown status"
+    assert L.spa2_status_str(8) == b"unknown status"
     assert L.spa2_num_blocks(32760, 128) == 256 and L.spa2_num_blocks(75600, 64) == 1182
     assert L.spa2_num_blocks(0, 64) == 0
 
@@ -175,3 +176,32 @@ def test_block_size_variants_accepted(bq, bkv):
     assert L.spa2_mask_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
     assert n.value > 0
     assert L.spa2_bwd_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
+
+
+ODD = C.c_void_p(0x1008)  # 8-byte aligned, not 16
+ODD4 = C.c_void_p(0x1002)  # not 4-byte aligned
+
+
+def test_misaligned_pointers():
+    """Pointers the kernels would load from with wider vector accesses than their alignment
+    allows are rejected before any HIP call."""
+    L = _lib.lib()
+    d = C.byref(good())
+    assert mask_call(q=ODD) == _lib.E_ALIGN
+    assert mask_call(out=bm(row_idx=ODD4)) == _lib.E_ALIGN
+    fargs = [FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None]  # q k v m o lse o_f32 stream
+    for i, bad in ((0, ODD), (2, ODD), (4, ODD), (5, ODD4), (6, ODD)):
+        a = list(fargs)
+        a[i] = bad
+        assert L.spa2_fwd(d, *a) == _lib.E_ALIGN, i
+    assert L.spa2_fwd(d, FAKE, FAKE, FAKE, C.byref(bm(col_cnt=ODD4)), FAKE, FAKE, None,
+                      None) == _lib.E_ALIGN
+    # q k v o o_f32 lse dout m dq dk dv ws ws_bytes stream
+    bargs = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 4 + [1 << 40, None]
+    for i, bad in ((1, ODD), (3, ODD), (5, ODD4), (6, ODD), (10, ODD), (11, ODD4)):
+        a = list(bargs)
+        a[i] = bad
+        assert L.spa2_bwd(d, *a) == _lib.E_ALIGN, i
+    assert L.spa2_select(d, ODD4, 0.1, 0.5, C.byref(bm()), None) == _lib.E_ALIGN
+    assert L.spa2_pool(d, FAKE, ODD, FAKE, FAKE, None) == _lib.E_ALIGN
+    assert L.spa2_mask_lists(d, C.byref(bm(row_cnt=ODD4)), None) == _lib.E_ALIGN
