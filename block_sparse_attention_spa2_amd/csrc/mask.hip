@@ -374,47 +374,76 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   if (l == 0) row_cnt[row] = rank;
 }
 
-// Row lists from a caller-filled mask (one thread per row).
-__global__ void rows_kernel(const uint8_t* __restrict__ mask, int rows, int Tn,
-                            int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
-  const uint8_t* m = mask + (size_t)r * Tn;
-  int32_t* out = row_idx + (size_t)r * Tn;
-  int c = 0;
-  for (int j = 0; j < Tn; ++j)
-    if (m[j]) out[c++] = j;
-  row_cnt[r] = c;
+// Row lists from a caller-filled mask: one wave per row, 64 blocks per step; a ballot of
+// the step's bytes (nonzero = kept) places every kept block after those of earlier steps.
+__global__ __launch_bounds__(256) void rows_kernel(const uint8_t* __restrict__ mask, int rows,
+                                                   int Tn, int32_t* __restrict__ row_cnt,
+                                                   int32_t* __restrict__ row_idx) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave leaves; no barrier below
+  const int l = lane_id();
+  const uint8_t* mr = mask + (size_t)row * Tn;
+  int32_t* out = row_idx + (size_t)row * Tn;
+  int base = 0;
+  for (int t0 = 0; t0 < Tn; t0 += 64) {
+    const int j = t0 + l;
+    const bool kb = j < Tn && mr[j] != 0;
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(kb);
+    if (kb)
+      out[base + __builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0))] = j;
+    base += __builtin_popcountll(bal);
+  }
+  if (l == 0) row_cnt[row] = base;
 }
 
-// Column lists: a workgroup covers 16 key blocks (columns) of one head; its 256 threads
-// are 16 columns x 16 slices of the query-block rows. Each thread counts its slice, the
-// counts are scanned over slices in LDS, and a second pass writes the ascending indices.
-__global__ __launch_bounds__(256) void cols_kernel(const uint8_t* __restrict__ mask, int Tm,
+// Column lists: a workgroup covers 64 key blocks (columns) of one head, one column per
+// lane; its eight waves take contiguous slices of the query blocks (rows), so every row's
+// 64 mask bytes are one coalesced load. Each wave counts its slice's kept rows per column,
+// the counts are scanned over the slices in LDS, and a second pass over the slice writes
+// the kept rows after those of the earlier slices: the lists come out ascending.
+__global__ __launch_bounds__(512) void cols_kernel(const uint8_t* __restrict__ mask, int Tm,
                                                    int Tn, int col_groups,
                                                    int32_t* __restrict__ col_cnt,
                                                    int32_t* __restrict__ col_idx) {
-  __shared__ int cnts[16][17];
+  constexpr int NWV = 8;  // waves (row slices) per workgroup
+  constexpr int U = 16;   // rows loaded together
+  __shared__ int cnts[NWV][64];
   const int bh = blockIdx.x / col_groups;
-  const int c = threadIdx.x & 15, part = threadIdx.x >> 4;
-  const int j = (blockIdx.x % col_groups) * 16 + c;
-  const int rp = (Tm + 15) / 16;
-  const int i0 = min(Tm, part * rp), i1 = min(Tm, i0 + rp);
-  const uint8_t* m = mask + (size_t)bh * Tm * Tn;
+  const int l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = (blockIdx.x % col_groups) * 64 + l;
+  const bool col_ok = j < Tn;
+  const int per = (Tm + NWV - 1) / NWV;
+  const int i0 = min(Tm, w * per), i1 = min(Tm, i0 + per);
+  const uint8_t* mc = mask + (size_t)bh * Tm * Tn + j;  // column j, row 0
+
   int n = 0;
-  if (j < Tn)
-#pragma unroll 8
-    for (int i = i0; i < i1; ++i) n += m[(size_t)i * Tn + j];
-  cnts[part][c] = n;
+  if (col_ok) {
+    for (int ib = i0; ib < i1; ib += U) {
+      // unconditional loads (row clamped into the slice) so all U are in flight together
+      uint8_t b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u] = mc[(size_t)min(ib + u, i1 - 1) * Tn];
+#pragma unroll
+      for (int u = 0; u < U; ++u) n += (ib + u < i1) & (b[u] != 0);
+    }
+  }
+  cnts[w][l] = n;
   __syncthreads();
   int off = 0;
-  for (int p = 0; p < part; ++p) off += cnts[p][c];
-  if (j < Tn) {
+  for (int v = 0; v < w; ++v) off += cnts[v][l];
+  if (col_ok) {
     int32_t* out = col_idx + ((size_t)bh * Tn + j) * Tm;
-#pragma unroll 8
-    for (int i = i0; i < i1; ++i)
-      if (m[(size_t)i * Tn + j]) out[off++] = i;
-    if (part == 15) col_cnt[(size_t)bh * Tn + j] = off;
+    for (int ib = i0; ib < i1; ib += U) {
+      uint8_t b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) b[u] = mc[(size_t)min(ib + u, i1 - 1) * Tn];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if ((ib + u < i1) & (b[u] != 0)) out[off++] = ib + u;
+    }
+    if (w == NWV - 1) col_cnt[(size_t)bh * Tn + j] = off;
   }
 }
 
@@ -543,13 +572,13 @@ hipError_t launch_orders(const OrderJob* a, const OrderJob* b, hipStream_t st) {
 
 hipError_t launch_rows(const Shape& s, const spa2_blockmask& m, hipStream_t st) {
   const int rows = s.BH() * s.Tm;
-  rows_kernel<<<(rows + 255) / 256, 256, 0, st>>>(m.mask, rows, s.Tn, m.row_cnt, m.row_idx);
+  rows_kernel<<<(rows + 3) / 4, 256, 0, st>>>(m.mask, rows, s.Tn, m.row_cnt, m.row_idx);
   return hipGetLastError();
 }
 
 hipError_t launch_cols(const Shape& s, const spa2_blockmask& m, hipStream_t st) {
-  const int groups = (s.Tn + 15) / 16;
-  cols_kernel<<<s.BH() * groups, 256, 0, st>>>(m.mask, s.Tm, s.Tn, groups, m.col_cnt, m.col_idx);
+  const int groups = (s.Tn + 63) / 64;
+  cols_kernel<<<s.BH() * groups, 512, 0, st>>>(m.mask, s.Tm, s.Tn, groups, m.col_cnt, m.col_idx);
   return hipGetLastError();
 }
 
