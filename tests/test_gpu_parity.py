@@ -155,12 +155,13 @@ def _crafted_pbar_rows(tn, n_rows, seed):
     return np.stack(rows[:n_rows])
 
 
-@pytest.mark.parametrize("n,seed", [(640, 0), (32768, 1), (5000, 2)])
+@pytest.mark.parametrize("n,seed", [(640, 0), (32768, 1), (5000, 2), (50000, 4), (262144, 3)])
 @pytest.mark.parametrize("kf,pf", [(0.2, 0.6), (0.02, 0.3), (0.1, 0.0), (0.0, 0.6), (0.5, 0.9)])
 def test_select_crafted_rows(n, seed, kf, pf):
     """The selection kernel on crafted P-bar rows (ties, equal high words, zeros) keeps
     exactly the oracle's blocks: both sides see the same values and sum the prefix in the
-    same rank order, so no band is excused. N = 640 gives the pages' 10-block rows."""
+    same rank order, so no band is excused. N = 640 gives the pages' 10-block rows; the
+    sizes cover rows of 8, 16 and 64 register rounds (T_n up to 4096, the largest)."""
     bq, bkv = 128, 64
     tm, tn = spa2.num_blocks(n, bq), spa2.num_blocks(n, bkv)
     pb = _crafted_pbar_rows(tn, tm, seed).reshape(1, 1, tm, tn)
