@@ -96,8 +96,9 @@ spa2_status hip_status(const char* where, hipError_t e) {
 // can hold most of the query blocks and must start first).
 spa2_status write_orders(const spa2::Shape& s, const spa2_blockmask& m, hipStream_t hs) {
   // rows head by head (per_head = T_m), columns by count over the whole range
-  const spa2::OrderJob rows{m.row_cnt, s.BH() * s.Tm, s.Tn, s.Tm, m.row_order};
-  const spa2::OrderJob cols{m.col_cnt, s.BH() * s.Tn, s.Tm, 0, m.col_order};
+  const spa2::OrderJob rows{m.row_cnt, s.BH() * s.Tm, s.Tn, s.Tm, 0, m.row_order};
+  const spa2::OrderJob cols{m.col_cnt, s.BH() * s.Tn, s.Tm, s.Tn, s.Tm / 4 > 1 ? s.Tm / 4 : 1,
+                            m.col_order};
   return hip_status("order", spa2::launch_orders(m.row_order ? &rows : nullptr,
                                                  m.col_order ? &cols : nullptr, hs));
 }

@@ -36,12 +36,14 @@ hipError_t launch_select(const Shape& s, const double* src, bool from_scores, do
                          int n_k, double p_frac, const spa2_blockmask& m, hipStream_t st);
 // A scheduling order to list: the kept counts of `items` lists (clamped to [0, maxc]),
 // written as a permutation to `order`; per_head > 0 groups the items head by head
-// (per_head items per head), 0 sorts the whole range by count.
+// (per_head items per head), 0 sorts the whole range by count; with per_head > 0, items
+// whose count reaches hoist (> 0) come first.
 struct OrderJob {
   const int32_t* cnt;
   int items;
   int maxc;
   int per_head;
+  int hoist;
   int32_t* order;
 };
 // One launch for up to two orders (either pointer may be NULL).

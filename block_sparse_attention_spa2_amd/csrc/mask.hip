@@ -505,7 +505,9 @@ hipError_t launch_select(const Shape& s, const double* src, bool from_scores, do
 // key is the kept count, largest first. With per_head > 0 (items per head) the part is
 // listed head by head, each head's items largest first, so the workgroups that run at the
 // same time on one XCD mostly read one head's tiles (more L2 reuse); if the part spans too
-// many heads for the histogram, the plain order is used. Items with equal keys land in the
+// many heads for the histogram, the plain order is used. With hoist > 0 as well, items
+// whose count reaches `hoist` are listed first (largest first) and only the rest head by
+// head, so that the few very long lists start at once. Items with equal keys land in the
 // order of their atomic increments.
 __global__ __launch_bounds__(256) void order_kernel(OrderJob j0, OrderJob j1) {
   constexpr int kBins = 16384;
@@ -516,19 +518,23 @@ __global__ __launch_bounds__(256) void order_kernel(OrderJob j0, OrderJob j1) {
   const OrderJob& job = blockIdx.x < 8 ? j0 : j1;
   const int32_t* __restrict__ cnt = job.cnt;
   int32_t* __restrict__ order = job.order;
-  const int items = job.items, maxc = job.maxc, per_head = job.per_head;
+  const int items = job.items, maxc = job.maxc, per_head = job.per_head, hoist = job.hoist;
   const int tid = threadIdx.x, x = blockIdx.x & 7;
   const int q = items >> 3, r = items & 7;
   const int lo = x * q + min(x, r), n = q + (x < r ? 1 : 0);
   const int nb = maxc + 1;
   const int h0 = per_head > 0 ? lo / per_head : 0;
   const int nh = per_head > 0 && n > 0 ? (lo + n - 1) / per_head - h0 + 1 : 1;
-  const bool by_head = nh * nb <= kBins;
-  const int nbins = by_head ? nh * nb : nb;
-  // bin of item lo + i: (head within the part, then count from the top)
+  const int top = per_head > 0 && hoist > 0 ? nb : 0;  // bins of the hoisted section
+  const bool by_head = top + nh * nb <= kBins;
+  const int nbins = by_head ? top + nh * nb : nb;
+  // bin of item lo + i: hoisted items by count from the top; the others by head within
+  // the part, then count from the top
   auto bin = [&](int i) {
     const int c = min(max(cnt[lo + i], 0), maxc);
-    return (by_head && per_head > 0 ? ((lo + i) / per_head - h0) * nb : 0) + (maxc - c);
+    if (!by_head || per_head == 0) return maxc - c;
+    if (top > 0 && c >= hoist) return maxc - c;
+    return top + ((lo + i) / per_head - h0) * nb + (maxc - c);
   };
   for (int c = tid; c < nbins; c += 256) hist[c] = 0;
   __syncthreads();

@@ -389,25 +389,30 @@ def _xcd_ranges(items):
 @pytest.mark.parametrize("name", ["ragged_bf16", "mid_bf16", "tiny_fp32"])
 def test_schedule_order(name):
     """row_order / col_order: each of the eight contiguous index ranges is a permutation of
-    itself; columns by kept count, non-increasing; rows head by head (heads ascending), each
-    head's rows by kept count; outputs do not depend on the order."""
+    itself. Rows head by head (heads ascending), each head's rows by kept count. Columns
+    kept by at least a quarter of the query blocks first, by count; then the others head by
+    head, each head's by count. Outputs do not depend on the order."""
     r = ref(name)
     d = r["dev"]
     bm = spa2.mask(d["q"], d["k"], r["k"], r["p"], r["bq"], r["bkv"])
     tm, tn = bm.mask.shape[-2:]
-    for cnt_t, ord_t, per_head in ((bm.row_cnt, bm.row_order, tm), (bm.col_cnt, bm.col_order, 0)):
+    for cnt_t, ord_t, per_head, hoist in ((bm.row_cnt, bm.row_order, tm, 0),
+                                          (bm.col_cnt, bm.col_order, tn, max(1, tm // 4))):
         cnt = cnt_t.cpu().numpy().reshape(-1)
         order = ord_t.cpu().numpy().reshape(-1)
         for lo, hi in _xcd_ranges(cnt.size):
             part = order[lo:hi]
             assert np.array_equal(np.sort(part), np.arange(lo, hi))
-            if per_head:
-                head = part // per_head
-                assert np.all(np.diff(head) >= 0)
-                same = np.diff(head) == 0
-                assert np.all(np.diff(cnt[part])[same] <= 0)
-            else:
-                assert np.all(np.diff(cnt[part]) <= 0)
+            c = np.minimum(cnt[part], tn if per_head == tm else tm)
+            n_top = int(np.sum(c >= hoist)) if hoist else 0
+            top, rest = part[:n_top], part[n_top:]
+            if hoist:
+                assert np.all(c[:n_top] >= hoist) and np.all(c[n_top:] < hoist)
+                assert np.all(np.diff(cnt[top]) <= 0)
+            head = rest // per_head
+            assert np.all(np.diff(head) >= 0)
+            same = np.diff(head) == 0
+            assert np.all(np.diff(cnt[rest])[same] <= 0)
     natural = spa2.BlockMask(bm.mask, bm.row_cnt, bm.row_idx, bm.col_cnt, bm.col_idx,
                              bm.bq, bm.bkv)
     of1 = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
