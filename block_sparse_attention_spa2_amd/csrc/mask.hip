@@ -75,69 +75,82 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
 
 // ------------------------------------------------------------------------------------
 // Pooled scores S-bar = q-bar k-bar^T / sqrt(D) on the fp64 matrix cores
-// (v_mfma_f64_16x16x4_f64). One wave per 16 x 32 output tile (two 16 x 16 MFMA tiles),
-// four consecutive tiles per workgroup, operands loaded straight into registers, no LDS
-// and no barrier. Lane (g, c) = (l / 16, l % 16) loads dims 8 i + 2 g and 8 i + 2 g + 1
-// of row c (A: query block, B: key block) with one 16-byte load, so the four lane groups
-// of a row read 64 contiguous bytes per load; those two dims feed reduction slot g at
-// steps 2 i and 2 i + 1. The dot product is the same sum in any slot order. Rows and keys
-// past the matrix read a clamped row and are not stored. `pitch` (doubles) is the row
-// stride of q-bar and k-bar: with rows exactly 1 KB apart the sixteen rows of one load
-// meet in a few L2 channels, and a pitch of D + 2 spreads them (measured: the operand
-// loads take 14 instead of 22 us at 12 x 256 x 512 blocks).
+// (v_mfma_f64_16x16x4_f64). One workgroup per 64 x 64 tile of one head (workgroups in
+// XCD-contiguous order, so an XCD's L2 holds the pooled vectors of its heads); wave w
+// computes rows 16 w .. 16 w + 15 against the 64 columns (four MFMA tiles). The reduction
+// runs over chunks of 16 dims: each chunk of q-bar and k-bar rows is loaded once per
+// workgroup (four threads per row, 32 contiguous bytes each) into a double-buffered LDS
+// stage while the previous chunk's products run. `pitch` (doubles) is the row stride of
+// q-bar and k-bar: rows exactly 1 KB apart meet in a few L2 channels, and a pitch of
+// D + 2 spreads them. Rows and keys past the matrix read a clamped row and are not stored.
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qbar,
                                                      const double* __restrict__ kbar,
                                                      double* __restrict__ scores, int Tm, int Tn,
-                                                     int pitch, int tiles_m, int tiles_n, int tiles,
+                                                     int pitch, int tiles_m, int tiles_n,
                                                      double sqrt_d) {
-  constexpr int NS = D / 4;  // MFMA steps (four dims each)
-  // XCD-contiguous workgroup order: an XCD covers a range of heads, whose pooled vectors
-  // then stay in its L2 for every tile that reads them
-  const int tile = xcd_item(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
-  if (tile >= tiles) return;  // whole wave leaves; no barrier below
-  const int l = lane_id(), g = l >> 4, c16 = l & 15;
+  constexpr int KC = 16;      // dims per chunk
+  constexpr int NC = D / KC;  // chunks
+  constexpr int LP = KC + 2;  // LDS row pitch in doubles (spreads rows over the banks)
+  __shared__ double sa[2][64 * LP];
+  __shared__ double sb[2][64 * LP];
+  const int tile = xcd_item(blockIdx.x, gridDim.x);
   const int per_head = tiles_m * tiles_n;
   const int bh = tile / per_head;
   const int tm = (tile % per_head) / tiles_n, tn = tile % tiles_n;
+  const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const double* qrow = qbar + ((size_t)bh * Tm + min(tm * 16 + c16, Tm - 1)) * pitch + 2 * g;
-  double a[NS], b[2][NS];
+  // loader: thread -> row lr of both tiles, dims lp .. lp + 3 of each chunk
+  const int lr = tid >> 2, lp = (tid & 3) * 4;
+  const double* qrow = qbar + ((size_t)bh * Tm + min(tm * 64 + lr, Tm - 1)) * pitch + lp;
+  const double* krow = kbar + ((size_t)bh * Tn + min(tn * 64 + lr, Tn - 1)) * pitch + lp;
+  f64x2 ra0, ra1, rb0, rb1;
+  auto gload = [&](int c) {
+    ra0 = *reinterpret_cast<const f64x2*>(qrow + c * KC);
+    ra1 = *reinterpret_cast<const f64x2*>(qrow + c * KC + 2);
+    rb0 = *reinterpret_cast<const f64x2*>(krow + c * KC);
+    rb1 = *reinterpret_cast<const f64x2*>(krow + c * KC + 2);
+  };
+  auto sstore = [&](int buf) {
+    double* a = sa[buf] + lr * LP + lp;
+    double* b = sb[buf] + lr * LP + lp;
+    a[0] = ra0[0]; a[1] = ra0[1]; a[2] = ra1[0]; a[3] = ra1[1];
+    b[0] = rb0[0]; b[1] = rb0[1]; b[2] = rb1[0]; b[3] = rb1[1];
+  };
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  f64x4 acc[4];
 #pragma unroll
-  for (int i = 0; i < NS / 2; ++i) {
-    const f64x2 x = *reinterpret_cast<const f64x2*>(qrow + 8 * i);
-    a[2 * i] = x[0];
-    a[2 * i + 1] = x[1];
-  }
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int c = 0; c < NC; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < NC) gload(c + 1);  // in flight during this chunk's products
+    const double* A = sa[buf] + (w * 16 + c16) * LP + g;
+    const double* Bm = sb[buf] + c16 * LP + g;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const double* krow = kbar + ((size_t)bh * Tn + min(tn * 32 + ct * 16 + c16, Tn - 1)) * pitch + 2 * g;
+    for (int st = 0; st < KC / 4; ++st) {
+      const double av = A[4 * st];
 #pragma unroll
-    for (int i = 0; i < NS / 2; ++i) {
-      const f64x2 x = *reinterpret_cast<const f64x2*>(krow + 8 * i);
-      b[ct][2 * i] = x[0];
-      b[ct][2 * i + 1] = x[1];
+      for (int ct = 0; ct < 4; ++ct)
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, Bm[ct * 16 * LP + 4 * st], acc[ct], 0, 0, 0);
     }
+    if (c + 1 < NC) sstore(buf ^ 1);  // that stage was last read before the previous barrier
+    __syncthreads();
   }
-  // every load is in flight before the first product (one memory round trip per wave)
-  __builtin_amdgcn_sched_barrier(0);
-  f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
-#pragma unroll
-  for (int i = 0; i < NS; ++i)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[ct][i], acc[ct], 0, 0, 0);
 
   // v_mfma_f64_16x16x4_f64 returns C[g + 4 e][l % 16] in element e of lane l (the fp32
   // results use 4 g + e instead).
   double* out = scores + (size_t)bh * Tm * Tn;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int col = tn * 32 + ct * 16 + c16;
+  for (int ct = 0; ct < 4; ++ct) {
+    const int col = tn * 64 + ct * 16 + c16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = tm * 16 + g + 4 * e;
+      const int row = tm * 64 + w * 16 + g + 4 * e;
       if (row < Tm && col < Tn) out[(size_t)row * Tn + col] = acc[ct][e] / sqrt_d;
     }
   }
@@ -467,14 +480,13 @@ hipError_t launch_pool(const Shape& s, const void* q, const void* k, double* qba
 
 hipError_t launch_scores(const Shape& s, const double* qbar, const double* kbar, int pitch,
                          double* scores, hipStream_t st) {
-  const int tm = (s.Tm + 15) / 16, tn = (s.Tn + 31) / 32;
-  const int tiles = s.BH() * tm * tn;  // one wave each, four per workgroup
-  const dim3 grid((tiles + 3) / 4);
+  const int tm = (s.Tm + 63) / 64, tn = (s.Tn + 63) / 64;
+  const dim3 grid(s.BH() * tm * tn);  // one workgroup per 64 x 64 tile
   const double sqrt_d = sqrt((double)s.D);
   if (s.D == 64)
-    scores_kernel<64><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, pitch, tm, tn, tiles, sqrt_d);
+    scores_kernel<64><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, pitch, tm, tn, sqrt_d);
   else
-    scores_kernel<128><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, pitch, tm, tn, tiles, sqrt_d);
+    scores_kernel<128><<<grid, 256, 0, st>>>(qbar, kbar, scores, s.Tm, s.Tn, pitch, tm, tn, sqrt_d);
   return hipGetLastError();
 }
 
