@@ -82,9 +82,13 @@ typedef struct {
  *   col_order int32 [B, H, T_n]      optional: the same for key blocks (dK/dV pass)
  * The forward reads the row lists; the backward reads both. The orders only schedule work
  * (results do not depend on them): the flattened block index range is cut into eight
- * contiguous parts (one per XCD of the GPU, sharing an L2 cache) and each part lists its
- * blocks by kept count, largest first, so that the longest rows start first; blocks of
- * equal count appear in no particular order. The mask calls write them when non-NULL. */
+ * contiguous parts (one per XCD of the GPU, sharing an L2 cache). A part of row_order
+ * lists its query blocks head by head, each head's by kept count, largest first (blocks
+ * running together on an XCD then read one head's key blocks). A part of col_order lists
+ * first the key blocks kept by at least a quarter of the query blocks (largest count
+ * first, so the longest lists start at once), then the others head by head, largest
+ * first. Blocks of equal count appear in no particular order. The mask calls write the
+ * orders when non-NULL. */
 typedef struct {
   uint8_t* mask;
   int32_t* row_cnt;
