@@ -478,3 +478,34 @@ def test_error_terms(name):
     print(f"[{name}] rel L1 {terms[..., 1].sum() / terms[..., 0].sum():.4f} = dropped "
           f"{terms[..., 2].sum() / terms[..., 0].sum():.4f} + renorm "
           f"{terms[..., 3].sum() / terms[..., 0].sum():.4f} (triangle)")
+
+
+def test_two_streams_concurrently():
+    """The library keeps no state between calls: two problems enqueued on two streams at
+    once (default priority) give bit-identical results to running them one after the
+    other on the default stream."""
+    ra, rb = ref("ragged_bf16"), ref("bq256_bf16")
+
+    def valid(idx, cnt):  # list entries past the count are unused
+        return idx[torch.arange(idx.shape[-1], device=idx.device) < cnt[..., None]]
+
+    def run(r):
+        d = r["dev"]
+        bm = spa2.mask(d["q"], d["k"], r["k"], r["p"], r["bq"], r["bkv"])
+        o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm)
+        grads = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm)
+        return [bm.mask, bm.row_cnt, bm.col_cnt, o, lse, *grads,
+                valid(bm.row_idx, bm.row_cnt), valid(bm.col_idx, bm.col_cnt)]
+
+    serial = [run(ra), run(rb)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.current_stream().synchronize()
+    with torch.cuda.stream(s1):
+        out_a = run(ra)
+    with torch.cuda.stream(s2):
+        out_b = run(rb)
+    torch.cuda.synchronize()
+    for want, got in zip(serial, (out_a, out_b)):
+        for x, y in zip(want, got):
+            assert torch.equal(x, y)
