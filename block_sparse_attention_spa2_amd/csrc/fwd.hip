@@ -66,7 +66,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pos = xcd_item(blockIdx.x, a.items);
+  // paired XCDs, unless a block runs as two tiles (they stay on one XCD, sharing its L2)
+  const int pos = a.qsub ? xcd_item(blockIdx.x, a.items) : xcd_item_paired(blockIdx.x, a.items);
   const int ppos = pos >> a.qsub;  // this query tile's block, in scheduling order
   const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[ppos]) : ppos;
   const int bh = item / a.Tm, qb = item % a.Tm;
