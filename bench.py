@@ -34,7 +34,7 @@ KERNEL_SOURCES = {
     "bwd_dkdv": ("bwd.hip", "common.h", "kernels.h"),
     "bwd_dq_rowterm": ("bwd.hip", "common.h", "kernels.h"),
 }
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_wan13b_480p.txt")
+TRAFFIC_PROFILES = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
 
 
 def log(*a):
@@ -64,9 +64,10 @@ def recorded_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's readings), or None when there is
     no record for this kernel and workload or the kernel changed since it was taken."""
-    if not os.path.exists(TRAFFIC_PROFILE):
+    path = TRAFFIC_PROFILES.format(workload=workload)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_PROFILE) as f:
+    with open(path) as f:
         for line in f:
             if not line.startswith("RECORD "):
                 continue
