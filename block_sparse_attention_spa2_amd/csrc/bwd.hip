@@ -90,23 +90,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 //   S^T = K Q^T, dP^T = V dO^T (A = K, V rows from LDS; B = Q, dO in registers),
 //   dS^T = P^T * (dP^T - Dv), dQ^T += K^T dS^T (A = K^T via transpose reads).
 //
-// bf16 only: two rounding errors grow with a large offset c_j shared by a block's keys (an
-// attention-sink block), because each is multiplied by the keys:
-//  * rounding dS to bf16 leaves sum_k r_k K_k, r = dS - bf16(dS), whose offset part
+// bf16 only: two rounding errors grow with a large component c_j shared by a block's keys
+// (an attention-sink block, or keys with a smooth positional component), because each is
+// multiplied by the keys:
+//  * rounding dS to bf16 leaves sum_k r_k K_k, r = dS - bf16(dS), whose c_j part
 //    (sum_k r_k) c_j is added back;
 //  * the row term Dv carries the rounding of O, which shifts every dS_k by -P_k dDv. In
 //    exact arithmetic sum_k dS_k = 0 over the row, so the measured T = sum_k dS_k equals
-//    -dDv, and the shift's offset part T sum_j P^blk_j c_j (P^blk_j = the row's mass on
+//    -dDv, and the shift's c_j part T sum_j P^blk_j c_j (P^blk_j = the row's mass on
 //    block j) is removed at the end.
-// c_j = the block's first key row; what remains involves only K_k - c_j. Both terms are
-// rank-one updates per block, w_j (x) c_j with w_j = sum_k r_k or P^blk_j. They are
-// batched on the matrix unit, eight blocks at a time: each lane group g (16 lanes, a
-// quarter of the block's keys) keeps its partial weights of the last eight blocks as the
-// eight reduction slots 8g .. 8g + 7 of an MFMA operand W, and an LDS matrix C holds c_j
-// of those blocks so that slot 8g + i of the other operand is c_i for every g. One MFMA
-// per output tile then sums the partials over the groups and the blocks: acc += C^T W,
-// pkc += C^T W'. The groups' partials of sum_k bf16(dS_k) come from the matrix unit too
-// (a 0/1 operand times the packed dS), so sum_k r_k costs one add per element.
+// What remains involves only K_k - c_j, so c_j is the block's mean key: it removes the
+// shared part whatever its shape (a first-key reference also carries that key's own
+// noise, which on keys with a smooth positional component left more error than no
+// correction at all). The mean comes from the matrix unit: each wave multiplies the K^T
+// fragments it reads for the dQ product by a constant 1/BKV operand for its share of the
+// head dimensions. Both terms are rank-one updates per block, w_j (x) c_j with
+// w_j = sum_k r_k or P^blk_j. They are batched on the matrix unit, eight blocks at a
+// time: each lane group g (16 lanes, a quarter of the block's keys) keeps its partial
+// weights of the last eight blocks as the eight reduction slots 8g .. 8g + 7 of an MFMA
+// operand W, and an LDS matrix C holds c_j of those blocks so that slot 8g + i of the
+// other operand is c_i for every g. One MFMA per output tile then sums the partials over
+// the groups and the blocks: acc += C^T W, pkc += C^T W'. The groups' partials of
+// sum_k bf16(dS_k) come from the matrix unit too (a 0/1 operand times the packed dS), so
+// sum_k r_k costs one add per element.
 // ------------------------------------------------------------------------------------
 template <typename T, int D, int BQ, int BKV, int KSUB, bool DENSE, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
@@ -119,7 +125,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   constexpr int DT = D / 16;
   using KV = Tile<T, BKV, D>;
   constexpr bool kCorr = sizeof(T) == 2;
-  using CM = Tile<T, 32, D>;  // c_j of one batch of 32 blocks (bf16 only)
+  using CM = Tile<T, 32, D>;  // c_j of one batch of eight blocks, four copies (bf16 only)
+  constexpr int MD = (DT + NW - 1) / NW;  // mean-key output tiles per wave
   // K/V stages in separate LDS variables, named statically (see the forward kernel). The
   // code also runs three stages (loads issued two blocks ahead, partial vmcnt waits), which
   // measured slower than two with eight waves per workgroup.
@@ -240,6 +247,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
   }
+  // B operand of 1/BKV (a power of two, exact in bf16): K^T times it is the block's mean
+  // key in every column
+  F inv_bkv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) inv_bkv[e] = (T)(1.0f / BKV);
 
   auto shift_in = [&](u32x4& r, float x) {  // drop element 0, append bf16(x) as element 7
     const unsigned b = __builtin_bit_cast(unsigned short, (bf16)x);
@@ -294,13 +306,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
       // shift registers' contents (this block has not shifted in yet)
       if (t > 0) take_pending();  // the previous block's weights
       if ((t & 7) == 0 && t > 0) flush(((t >> 3) & 1) ? cm0 : cm1);
-      // this block's first key row, four copies (one per lane group)
-      if (w == 0) {
-        const int i = t & 7, c = l & 15, gg = l >> 4;
-        const int row = (i < 4 ? i : 12 + i) + 4 * gg;
-        char* cmw = ((t >> 3) & 1) ? cm1 : cm0;
-        CM::store_chunk(cmw, row, c, *reinterpret_cast<const u32x4*>(Kb + KV::offset(0, c * 8)));
-      }
     }
 
     f32x4 s[KTN][QT], dp[KTN][QT];
@@ -355,6 +360,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     f32x4 cs[QT];  // element g: sum of bf16(dS_k) over this lane group's keys
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) cs[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the block's mean key for this wave's share of the head dimensions (output tiles
+    // dt = w, w + NW, ...): lane holds mean[16 dt + 4 g + e] (every column the same)
+    f32x4 cmean[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) cmean[md] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < UPV; ++u) {
       F pf[QT];
@@ -370,6 +380,24 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
         KV::read_col4(Kb, 32 * u + 16, dt * 16, kt_, 1);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = E::mma(kt_, pf[qt], acc[dt][qt]);
+        if (kCorr && dt % NW == w) cmean[dt / NW] = E::mma(kt_, inv_bkv, cmean[dt / NW]);
+      }
+    }
+    if constexpr (kCorr) {
+      // C rows of block i = t mod 8: rows 4 g' + i (i < 4) or 16 + 4 g' + (i - 4) for the
+      // four copies g' = 0..3, written by lanes 0..3 (lane g' writes copy g'); visible to
+      // every wave after the next block's barrier, before the batch's flush reads them
+      if (c16 < 4) {
+        const int i = t & 7;
+        const int row = (i < 4 ? i : 12 + i) + 4 * c16;
+        char* cmw = ((t >> 3) & 1) ? cm1 : cm0;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const int dt = md * NW + w;
+          if (dt < DT)
+            *reinterpret_cast<bf16x4*>(cmw + CM::offset(row, dt * 16 + 4 * g)) =
+                bf16x4{(bf16)cmean[md][0], (bf16)cmean[md][1], (bf16)cmean[md][2], (bf16)cmean[md][3]};
+        }
       }
     }
     if constexpr (kCorr) {
