@@ -37,6 +37,7 @@ SIGNATURES = {
     "spa2_mask_lists": (C.c_int, [_DESC, _BM, _P]),
     "spa2_fwd": (C.c_int, [_DESC, _P, _P, _P, _BM, _P, _P, _P, _P]),
     "spa2_bwd_workspace_size": (C.c_int, [_DESC, C.POINTER(_SZ)]),
+    "spa2_bwd_workspace_bytes": (_SZ, [_DESC]),
     "spa2_bwd": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P, _P, _SZ, _P]),
     "spa2_bwd_prep": (C.c_int, [_DESC, _P, _P, _P, _P, _P]),
     "spa2_bwd_dkdv": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P]),

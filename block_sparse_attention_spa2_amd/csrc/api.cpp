@@ -228,6 +228,11 @@ spa2_status spa2_bwd_workspace_size(const spa2_desc* desc, size_t* bytes) {
   return SPA2_OK;
 }
 
+size_t spa2_bwd_workspace_bytes(const spa2_desc* desc) {
+  size_t bytes = 0;
+  return spa2_bwd_workspace_size(desc, &bytes) == SPA2_OK ? bytes : 0;
+}
+
 spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const void* v,
                      const void* o, const float* o_f32, const float* lse, const void* dout,
                      const spa2_blockmask* m, void* dq, void* dk, void* dv, void* workspace,

@@ -158,6 +158,12 @@ spa2_status spa2_fwd(const spa2_desc* desc, const void* q, const void* k, const 
 /* Workspace bytes that spa2_bwd needs (the per-row dot(dO, O) vector, float). */
 spa2_status spa2_bwd_workspace_size(const spa2_desc* desc, size_t* bytes);
 
+/* The same size as a plain return value: B * H * N * 4 bytes for a valid descriptor, 0 for
+ * an invalid one (or NULL), which spa2_bwd then rejects with its own status. The backward
+ * is deterministic and always needs this buffer: its dK/dV pass reads the row term
+ * rowsum(dO * O) that the dQ pass stores there. */
+size_t spa2_bwd_workspace_bytes(const spa2_desc* desc);
+
 /* Backward of spa2_fwd with the same mask held fixed (the mask gets no gradient):
  *   dP = dO V^T, dS = P * (dP - rowsum(dO * O)), dQ = dS K / sqrt(D),
  *   dK = dS^T Q / sqrt(D), dV = P^T dO, over kept pairs only, with P rebuilt from LSE.

@@ -157,6 +157,20 @@ def test_workspace_checks():
     assert L.spa2_bwd(C.byref(d), *head, None, n.value, None) == _lib.E_WORKSPACE
 
 
+def test_bwd_workspace_bytes():
+    """The size as a return value equals the status-returning size call for every valid
+    descriptor, and is 0 for an invalid descriptor or NULL."""
+    L = _lib.lib()
+    n = C.c_size_t(0)
+    for kw in (dict(), dict(B=2, H=3, N=777, D=64, dtype=_lib.F32), dict(N=75600, H=40)):
+        d = good(**kw)
+        assert L.spa2_bwd_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
+        assert L.spa2_bwd_workspace_bytes(C.byref(d)) == n.value == d.B * d.H * d.N * 4
+    assert L.spa2_bwd_workspace_bytes(C.byref(good(D=96))) == 0
+    assert L.spa2_bwd_workspace_bytes(C.byref(good(dtype=9))) == 0
+    assert L.spa2_bwd_workspace_bytes(None) == 0
+
+
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
     """The Python layer has no fallback: a missing library is an import-time error."""
     monkeypatch.setattr(_lib, "_lib", None)
