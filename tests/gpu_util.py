@@ -28,13 +28,20 @@ def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-def check_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str) -> dict:
-    """bf16: relative L2 bar; fp32: max-abs bar. A reference that is exactly zero (e.g. the
-    gradients of a row whose single kept key takes all the weight) has no relative scale
-    and is held to the fp32 max-abs bar instead."""
+def _segments(shape, block):
+    """Row segments of a [..., N, D] array: every block of `block` rows (the last one
+    partial) of every leading index (head)."""
+    n = shape[-2]
+    lead = int(np.prod(shape[:-2])) if len(shape) > 2 else 1
+    for hh in range(lead):
+        for lo in range(0, n, block):
+            yield hh, lo, min(n, lo + block)
+
+
+def _check_one(name, got, ref, dtype):
     tol = TOL[dtype]
-    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-    stats = dict(max_abs=float(np.abs(got - ref).max()), rel_l2=rel_l2(got, ref))
+    stats = dict(max_abs=float(np.abs(got - ref).max()) if got.size else 0.0,
+                 rel_l2=rel_l2(got, ref))
     if not np.any(ref):
         assert stats["max_abs"] <= TOL["f32"]["max_abs"], f"{name} (zero reference): {stats}"
         return stats
@@ -42,6 +49,39 @@ def check_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str) -> dict
         assert stats["rel_l2"] <= tol["rel_l2"], f"{name}: {stats}"
     else:
         assert stats["max_abs"] <= tol["max_abs"], f"{name}: {stats}"
+    return stats
+
+
+def check_close(name: str, got: np.ndarray, ref: np.ndarray, dtype: str, block=None) -> dict:
+    """bf16: relative L2 bar; fp32: max-abs bar. A reference that is exactly zero (e.g. the
+    gradients of a row whose single kept key takes all the weight) has no relative scale
+    and is held to the fp32 max-abs bar instead.
+
+    The bar holds for the whole tensor and, when `block` is given, for every block on its
+    own, so that one wrong row or block cannot hide in a whole-tensor norm:
+      block = int:  rows per block along axis -2 of a [..., N, D] array (the query block
+                    size for O and dQ, the key block size for dK and dV), per head;
+      block = list: explicit row-index arrays into axis 0 of a 2-D array (sampled blocks).
+    The returned stats carry the worst block's relative L2 as `block_rel_l2`."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    stats = _check_one(name, got, ref, dtype)
+    if block is None:
+        return stats
+    worst = 0.0
+    if isinstance(block, int):
+        g = got.reshape(-1, *got.shape[-2:])
+        r = ref.reshape(-1, *ref.shape[-2:])
+        segs = ((f"{name}[head {hh} rows {lo}:{hi}]", g[hh, lo:hi], r[hh, lo:hi])
+                for hh, lo, hi in _segments(got.shape, block))
+    else:
+        segs = ((f"{name}[rows {int(ix[0])}..{int(ix[-1])}]", got[ix], ref[ix])
+                for ix in block if len(ix))
+    for nm, gb, rb in segs:
+        st = _check_one(nm, gb, rb, dtype)
+        if np.any(rb):
+            worst = max(worst, st["rel_l2"])
+    stats["block_rel_l2"] = worst
     return stats
 
 

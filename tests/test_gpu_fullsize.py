@@ -40,33 +40,52 @@ def test_wan13b_mask_all_heads(wan13b):
     assert abs(wan13b["mask"].mean() - 0.05) < 1e-4
 
 
+def _oracle_lists(mask, like, bq, bkv):
+    """Row/column lists and scheduling orders of the oracle's own mask, built by the
+    library's list kernels (so the attention check does not depend on the GPU mask)."""
+    return spa2.mask_lists(torch.from_numpy(mask.astype(np.uint8)).cuda(), like, bq, bkv)
+
+
+def _rows(blocks, b, n):
+    return [np.arange(i * b, min(n, (i + 1) * b)) for i in blocks]
+
+
 def test_wan13b_fwd_bwd_sampled(wan13b):
+    """Forward and backward on the oracle's mask at the 480p shape, in the benchmark's
+    launch configuration; O, LSE and dQ on three query blocks of every head (the first,
+    the partial last and a random one), dK and dV on two or three key blocks (the partial
+    last, a random one, and the sink block 0 on two heads), each block held to the bar on
+    its own."""
     w, d, inp = wan13b["w"], wan13b["dev"], wan13b["inp"]
     bq, bkv, N = w["BQ"], w["BKV"], w["N"]
-    bm = spa2.mask(d["q"], d["k"], w["k"], w["p"], bq, bkv)
-    gm = bm.mask.cpu().numpy().astype(bool)
+    om = wan13b["mask"]
+    bm = _oracle_lists(om, d["q"], bq, bkv)
     of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
     o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
     dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
     on, ln = gu.to_f64(o), lse.cpu().numpy().astype(np.float64)
     dqn, dkn, dvn = gu.to_f64(dq), gu.to_f64(dk), gu.to_f64(dv)
-    tm, tn = gm.shape[-2:]
+    tm, tn = om.shape[-2:]
     rng = np.random.default_rng(0)
+    worst = {}
     for h in range(w["H"]):
-        m = gm[0, h]
+        m = om[0, h]
         q, k, v, do = (inp.head_f64(x, 0, h) for x in ("q", "k", "v", "do"))
         qblocks = sorted({0, tm - 1, int(rng.integers(tm))})
         kblocks = sorted({tn - 1, int(rng.integers(1, tn - 1))} | ({0} if h < 2 else set()))
         rows = sorted(set(qblocks) | {i for j in kblocks for i in np.flatnonzero(m[:, j])})
         o_ref, lse_ref = oracle.attn_fwd_head(q, k, v, m, bq, bkv, rows=qblocks)
         dq_ref, dk_ref, dv_ref = oracle.attn_bwd_head(q, k, v, do, m, bq, bkv, rows=rows)
-        qr = np.concatenate([np.arange(i * bq, min(N, (i + 1) * bq)) for i in qblocks])
-        kr = np.concatenate([np.arange(j * bkv, min(N, (j + 1) * bkv)) for j in kblocks])
-        gu.check_close(f"O h{h}", on[0, h][qr], o_ref[qr], "bf16")
+        qseg, kseg = _rows(qblocks, bq, N), _rows(kblocks, bkv, N)
+        qr, kr = np.concatenate(qseg), np.concatenate(kseg)
+        qloc = np.split(np.arange(qr.size), np.cumsum([x.size for x in qseg])[:-1])
+        kloc = np.split(np.arange(kr.size), np.cumsum([x.size for x in kseg])[:-1])
+        for nm, got, want, idx, loc in (("O", on, o_ref, qr, qloc), ("dQ", dqn, dq_ref, qr, qloc),
+                                        ("dK", dkn, dk_ref, kr, kloc), ("dV", dvn, dv_ref, kr, kloc)):
+            st = gu.check_close(f"{nm} h{h}", got[0, h][idx], want[idx], "bf16", block=loc)
+            worst[nm] = max(worst.get(nm, 0.0), st["block_rel_l2"])
         gu.check_lse(ln[0, h][qr], lse_ref[qr], "bf16")
-        gu.check_close(f"dQ h{h}", dqn[0, h][qr], dq_ref[qr], "bf16")
-        gu.check_close(f"dK h{h}", dkn[0, h][kr], dk_ref[kr], "bf16")
-        gu.check_close(f"dV h{h}", dvn[0, h][kr], dv_ref[kr], "bf16")
+    print(f"[wan13b_480p] worst block rel L2: {worst}")
 
 
 def test_staged_backward_equals_bwd(wan13b):
@@ -138,20 +157,26 @@ def test_wan14b_mask_all_heads(wan14b):
 
 
 def test_wan14b_fwd_sampled(wan14b):
-    """Forward at the 720p shape (591 x 1182 block grid, q tail 80 rows, k tail 16 keys)
-    on three query blocks of every head, including the partial last one."""
+    """Forward at the 720p shape (591 x 1182 block grid, q tail 80 rows, k tail 16 keys) on
+    the oracle's mask, three query blocks of every head including the partial last one,
+    each block held to the bar on its own."""
     w, d, inp = wan14b["w"], wan14b["dev"], wan14b["inp"]
     bq, bkv, N = w["BQ"], w["BKV"], w["N"]
-    bm = spa2.mask(d["q"], d["k"], w["k"], w["p"], bq, bkv)
-    gm = bm.mask.cpu().numpy().astype(bool)
+    om = wan14b["mask"]
+    bm = _oracle_lists(om, d["q"], bq, bkv)
     o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm)
     on, ln = gu.to_f64(o), lse.cpu().numpy().astype(np.float64)
-    tm = gm.shape[-2]
+    tm = om.shape[-2]
     rng = np.random.default_rng(1)
+    worst = 0.0
     for h in range(w["H"]):
         q, k, v = (inp.head_f64(x, 0, h) for x in ("q", "k", "v"))
         qblocks = sorted({0, tm - 1, int(rng.integers(tm))})
-        o_ref, lse_ref = oracle.attn_fwd_head(q, k, v, gm[0, h], bq, bkv, rows=qblocks)
-        qr = np.concatenate([np.arange(i * bq, min(N, (i + 1) * bq)) for i in qblocks])
-        gu.check_close(f"O h{h}", on[0, h][qr], o_ref[qr], "bf16")
+        o_ref, lse_ref = oracle.attn_fwd_head(q, k, v, om[0, h], bq, bkv, rows=qblocks)
+        qseg = _rows(qblocks, bq, N)
+        qr = np.concatenate(qseg)
+        loc = np.split(np.arange(qr.size), np.cumsum([x.size for x in qseg])[:-1])
+        st = gu.check_close(f"O h{h}", on[0, h][qr], o_ref[qr], "bf16", block=loc)
+        worst = max(worst, st["block_rel_l2"])
         gu.check_lse(ln[0, h][qr], lse_ref[qr], "bf16")
+    print(f"[wan14b_720p] worst block rel L2 of O: {worst:.2e}")

@@ -181,7 +181,7 @@ def test_fwd(name):
     r = ref(name)
     bm = _oracle_bm(r)
     o, lse = spa2.fwd(r["dev"]["q"], r["dev"]["k"], r["dev"]["v"], bm)
-    st = gu.check_close("O", gu.to_f64(o), r["o"], r["inp"].dtype)
+    st = gu.check_close("O", gu.to_f64(o), r["o"], r["inp"].dtype, block=r["bq"])
     e = gu.check_lse(lse.cpu().numpy().astype(np.float64), r["lse"], r["inp"].dtype)
     print(f"[{name}] fwd O {st} LSE {e:.2e}")
 
@@ -195,8 +195,9 @@ def test_bwd(name):
     o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
     dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
     out = {}
-    for nm, got, want in (("dQ", dq, r["dq"]), ("dK", dk, r["dk"]), ("dV", dv, r["dv"])):
-        out[nm] = gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
+    for nm, got, want, blk in (("dQ", dq, r["dq"], r["bq"]), ("dK", dk, r["dk"], r["bkv"]),
+                               ("dV", dv, r["dv"], r["bkv"])):
+        out[nm] = gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype, block=blk)
     print(f"[{name}] bwd {out}")
 
 
@@ -211,9 +212,10 @@ def test_end_to_end_mask_fwd_bwd(name):
     of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
     o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
     dq, dk, dv = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
-    gu.check_close("O", gu.to_f64(o), r["o"], r["inp"].dtype)
-    for nm, got, want in (("dQ", dq, r["dq"]), ("dK", dk, r["dk"]), ("dV", dv, r["dv"])):
-        gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
+    gu.check_close("O", gu.to_f64(o), r["o"], r["inp"].dtype, block=r["bq"])
+    for nm, got, want, blk in (("dQ", dq, r["dq"], r["bq"]), ("dK", dk, r["dk"], r["bkv"]),
+                               ("dV", dv, r["dv"], r["bkv"])):
+        gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype, block=blk)
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_bf16_d64", "bkv32_bf16",
@@ -237,11 +239,12 @@ def test_dense_path(name):
     q, k, v, do = (r["inp"].f64(x) for x in ("q", "k", "v", "do"))
     allm = np.ones((B, H) + tuple(ones.shape[2:]), dtype=bool)
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, allm, r["bq"], r["bkv"])
-    gu.check_close("O dense", gu.to_f64(o1), o_ref, r["inp"].dtype)
+    gu.check_close("O dense", gu.to_f64(o1), o_ref, r["inp"].dtype, block=r["bq"])
     gu.check_lse(l1.cpu().numpy().astype(np.float64), lse_ref, r["inp"].dtype)
     dq, dk, dv = oracle.attn_bwd(q, k, v, do, allm, r["bq"], r["bkv"])
-    for nm, got, want in (("dQ", g1[0], dq), ("dK", g1[1], dk), ("dV", g1[2], dv)):
-        gu.check_close(nm + " dense", gu.to_f64(got), want, r["inp"].dtype)
+    for nm, got, want, blk in (("dQ", g1[0], dq, r["bq"]), ("dK", g1[1], dk, r["bkv"]),
+                               ("dV", g1[2], dv, r["bkv"])):
+        gu.check_close(nm + " dense", gu.to_f64(got), want, r["inp"].dtype, block=blk)
 
 
 @pytest.mark.parametrize("kf,pf", [(1.0, 0.0), (0.0, 1.0), (0.0, 0.3), (0.3, 0.0), (0.01, 0.9),
@@ -275,10 +278,11 @@ def test_empty_rows():
     on, ln = gu.to_f64(o), lse.cpu().numpy().astype(np.float64)
     assert np.all(on[0, 1, 384:512] == 0) and np.all(np.isneginf(ln[0, 1, 384:512]))
     assert np.all(gu.to_f64(dq)[0, 1, 384:512] == 0)
-    gu.check_close("O", on, o_ref, "bf16")
+    gu.check_close("O", on, o_ref, "bf16", block=r["bq"])
     gu.check_lse(ln, lse_ref, "bf16")
-    for nm, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
-        gu.check_close(nm, gu.to_f64(got), want, "bf16")
+    for nm, got, want, blk in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs,
+                                  (r["bq"], r["bkv"], r["bkv"])):
+        gu.check_close(nm, gu.to_f64(got), want, "bf16", block=blk)
 
 
 def test_deterministic_and_in_bounds():
@@ -314,7 +318,7 @@ def test_deterministic_and_in_bounds():
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "mid_bf16", "ragged_bf16_d64", "bkv32_bf16",
-                                  "bq256_bkv128_d64_bf16"])
+                                  "bq256_bkv128_d64_bf16", "bq64_bkv32_d64_bf16"])
 def test_bwd_without_unrounded_o(name):
     """The backward also accepts only the rounded O (row term from bf16 O): the dQ pass's
     shift correction removes the offset part of the row term's rounding, so the result
@@ -328,10 +332,11 @@ def test_bwd_without_unrounded_o(name):
     o2, lse2 = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
     g2 = spa2.bwd(d["q"], d["k"], d["v"], o2, lse2, d["do"], bm, o_f32=of)
     out = {}
-    for nm, got, got2, want in (("dQ", dq, g2[0], r["dq"]), ("dK", dk, g2[1], r["dk"]),
-                                ("dV", dv, g2[2], r["dv"])):
-        e1 = gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)["rel_l2"]
-        e2 = gu.check_close(nm, gu.to_f64(got2), want, r["inp"].dtype)["rel_l2"]
+    for nm, got, got2, want, blk in (("dQ", dq, g2[0], r["dq"], r["bq"]),
+                                     ("dK", dk, g2[1], r["dk"], r["bkv"]),
+                                     ("dV", dv, g2[2], r["dv"], r["bkv"])):
+        e1 = gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype, block=blk)["rel_l2"]
+        e2 = gu.check_close(nm, gu.to_f64(got2), want, r["inp"].dtype, block=blk)["rel_l2"]
         out[nm] = (round(e1, 5), round(e2, 5))
         assert e1 <= 2 * e2 + 1e-3, (nm, e1, e2)
     print(f"[{name}] rel L2 (bf16 O, unrounded O): {out}")
@@ -363,8 +368,9 @@ def test_staged_backward(name):
     dk3, dv3 = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm,
                              torch.empty_like(o), torch.empty_like(o))
     dq3 = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm, torch.empty_like(o))
-    for nm, got, want in (("dQ", dq3, r["dq"]), ("dK", dk3, r["dk"]), ("dV", dv3, r["dv"])):
-        gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype)
+    for nm, got, want, blk in (("dQ", dq3, r["dq"], r["bq"]), ("dK", dk3, r["dk"], r["bkv"]),
+                               ("dV", dv3, r["dv"], r["bkv"])):
+        gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype, block=blk)
 
 
 def test_o_f32_is_unrounded_o():
@@ -374,7 +380,7 @@ def test_o_f32_is_unrounded_o():
     of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
     o, _ = spa2.fwd(d["q"], d["k"], d["v"], _oracle_bm(r), o_f32=of)
     assert torch.equal(of.to(torch.bfloat16), o)
-    gu.check_close("O f32", of.cpu().numpy().astype(np.float64), r["o"], "bf16")
+    gu.check_close("O f32", of.cpu().numpy().astype(np.float64), r["o"], "bf16", block=r["bq"])
 
 
 def _xcd_ranges(items):
