@@ -16,8 +16,8 @@ import torch
 from . import _lib
 from ._lib import Spa2Error  # noqa: F401
 
-__all__ = ["BlockMask", "pool", "mask", "select", "mask_lists", "fwd", "bwd", "bwd_prep",
-           "bwd_dkdv", "bwd_dq", "bwd_dq_rowterm", "error_terms",
+__all__ = ["BlockMask", "pool", "mask", "select", "mask_lists", "fwd", "bwd", "bwd_noalloc",
+           "bwd_prep", "bwd_dkdv", "bwd_dq", "bwd_dq_rowterm", "error_terms",
            "mask_workspace_size", "bwd_workspace_size", "num_blocks", "Spa2Error"]
 
 
@@ -242,6 +242,31 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
         C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_f32), _ptr(lse),
         _ptr(do), bmc, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
         _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                lse: torch.Tensor, do: torch.Tensor, bm: BlockMask | None, out: tuple,
+                bq: int = 128, bkv: int = 64, *, o_f32: torch.Tensor | None = None):
+    """bwd() through spa2_bwd_noalloc: no workspace (the library's built-in scratch holds
+    the row term), outputs given by the caller in `out` = (dQ, dK, dV). Calls that overlap
+    on one GPU share that scratch and must be serialised."""
+    if bm is not None:
+        bq, bkv = bm.bq, bm.bkv
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _expect(name, t, q.shape, q.dtype)
+    _expect("lse", lse, q.shape[:3], torch.float32)
+    if o_f32 is not None:
+        _expect("o_f32", o_f32, q.shape, torch.float32)
+    if bm is not None:
+        _check_bm(bm, q)
+    dq, dk, dv = out
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(name, t, q.shape, q.dtype)
+    bmc = C.byref(bm.c()) if bm is not None else None
+    _lib.check("spa2_bwd_noalloc", _lib.lib().spa2_bwd_noalloc(
+        C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_f32), _ptr(lse),
+        _ptr(do), bmc, _ptr(dq), _ptr(dk), _ptr(dv), _stream(q)))
     return dq, dk, dv
 
 

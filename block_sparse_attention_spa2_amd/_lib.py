@@ -7,7 +7,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libspa2.so")
 
-OK, E_NULL, E_SHAPE, E_DTYPE, E_PARAM, E_WORKSPACE, E_HIP, E_ALIGN = range(8)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_PARAM, E_WORKSPACE, E_HIP, E_ALIGN, E_SCRATCH = range(9)
+NOALLOC_SCRATCH_BYTES = 16 << 20  # SPA2_NOALLOC_SCRATCH_BYTES
 F32, BF16 = 0, 1
 
 
@@ -39,6 +40,7 @@ SIGNATURES = {
     "spa2_bwd_workspace_size": (C.c_int, [_DESC, C.POINTER(_SZ)]),
     "spa2_bwd_workspace_bytes": (_SZ, [_DESC]),
     "spa2_bwd": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P, _P, _SZ, _P]),
+    "spa2_bwd_noalloc": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P, _P]),
     "spa2_bwd_prep": (C.c_int, [_DESC, _P, _P, _P, _P, _P]),
     "spa2_bwd_dkdv": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P]),
     "spa2_bwd_dq": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _BM, _P, _P]),

@@ -6,9 +6,16 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/spa2.h"
 #include "kernels.h"
+
+// Scratch memory of spa2_bwd_noalloc (the backward's row term, float per query row), for
+// callers that cannot allocate. Every GPU the library runs on holds its own copy until the
+// process ends. In host code `scratch` is only a stand-in for the symbol: its device
+// address comes from hipGetSymbolAddress (scratch_on_device below).
+static __device__ __align__(256) unsigned char scratch[SPA2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -103,6 +110,38 @@ spa2_status write_orders(const spa2::Shape& s, const spa2_blockmask& m, hipStrea
                                                  m.col_order ? &cols : nullptr, hs));
 }
 
+// Device address of `scratch` on the device that runs `stream`, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+spa2_status scratch_on_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_status("hipStreamGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "scratch: device %d out of range", dev);
+    return SPA2_E_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status("hipGetDevice", e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status("hipSetDevice", e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_status("hipGetSymbolAddress(scratch)", e);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SPA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +156,7 @@ const char* spa2_status_str(spa2_status s) {
     case SPA2_E_WORKSPACE: return "workspace missing or too small";
     case SPA2_E_HIP: return "HIP runtime error";
     case SPA2_E_ALIGN: return "a device pointer is not aligned for the kernels' vector loads";
+    case SPA2_E_SCRATCH: return "problem too large for the built-in scratch of the no-allocation call";
   }
   return "unknown status";
 }
@@ -249,6 +289,25 @@ spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const 
   return hip_status("bwd", spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, dk, dv,
                                             (float*)workspace, spa2::kBwdDqRow | spa2::kBwdDkdv,
                                             (hipStream_t)stream));
+}
+
+spa2_status spa2_bwd_noalloc(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                             const void* o, const float* o_f32, const float* lse,
+                             const void* dout, const spa2_blockmask* m, void* dq, void* dk,
+                             void* dv, void* stream) {
+  spa2::Shape s;
+  spa2_status st = check_desc(desc, &s);
+  if (st != SPA2_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPA2_E_NULL;
+  if (m && (!m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
+  if (!aligned16({q, k, v, o, o_f32, dout, dq, dk, dv}) || !aligned4({lse}) || !lists_aligned(m))
+    return SPA2_E_ALIGN;
+  if ((size_t)s.BH() * s.N * sizeof(float) > (size_t)SPA2_NOALLOC_SCRATCH_BYTES) return SPA2_E_SCRATCH;
+  const hipStream_t hs = (hipStream_t)stream;
+  void* ws = nullptr;
+  if ((st = scratch_on_device(hs, &ws)) != SPA2_OK) return st;
+  return hip_status("bwd_noalloc", spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, dk, dv,
+                                                    (float*)ws, spa2::kBwdDqRow | spa2::kBwdDkdv, hs));
 }
 
 spa2_status spa2_bwd_dq_rowterm(const spa2_desc* desc, const void* q, const void* k,

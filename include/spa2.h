@@ -58,7 +58,8 @@ typedef enum {
   SPA2_E_PARAM = 4,     /* k or p outside [0, 1], NaN, or both zero */
   SPA2_E_WORKSPACE = 5, /* workspace NULL or smaller than the size call reports */
   SPA2_E_HIP = 6,       /* a HIP runtime call or kernel launch failed */
-  SPA2_E_ALIGN = 7      /* a device pointer is not aligned as the conventions require */
+  SPA2_E_ALIGN = 7,     /* a device pointer is not aligned as the conventions require */
+  SPA2_E_SCRATCH = 8    /* too large for the built-in scratch of spa2_bwd_noalloc */
 } spa2_status;
 
 typedef enum { SPA2_F32 = 0, SPA2_BF16 = 1 } spa2_dtype;
@@ -175,6 +176,25 @@ spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const 
                      const void* o, const float* o_f32, const float* lse, const void* dout,
                      const spa2_blockmask* m, void* dq, void* dk, void* dv, void* workspace,
                      size_t ws_bytes, void* stream);
+
+/* Bytes of device scratch that spa2_bwd_noalloc holds per GPU: the row term of up to
+ * 4,194,304 query rows (B * H * N), e.g. 40 heads of 75,600 tokens. */
+#define SPA2_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* spa2_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid allocation). The
+ * row term goes to a scratch array built into the library (SPA2_NOALLOC_SCRATCH_BYTES per
+ * GPU, held until the process ends); the call itself allocates nothing. Same arguments,
+ * kernels and results as spa2_bwd (bit for bit). Returns SPA2_E_SCRATCH, before any HIP
+ * call, when B * H * N * 4 bytes exceed the scratch. The scratch is shared by every call on
+ * a GPU and keeps the last call's contents (nothing in it needs clearing: the dQ pass
+ * writes every row term before the dK/dV pass reads it), so calls that overlap on one GPU
+ * (other streams, other threads) race: serialise them. The first call on a device looks
+ * up the scratch address there (hipGetSymbolAddress on the stream's device). */
+spa2_status spa2_bwd_noalloc(const spa2_desc* desc, const void* q, const void* k, const void* v,
+                             const void* o, const float* o_f32, const float* lse,
+                             const void* dout, const spa2_blockmask* m, void* dq, void* dk,
+                             void* dv, void* stream);
 
 /* The passes of spa2_bwd, callable one by one (for example to time them, or to run the
  * dK/dV pass on another stream). spa2_bwd is exactly spa2_bwd_dq_rowterm, then

@@ -53,9 +53,9 @@ def mask_call(desc=None, q=FAKE, k=FAKE, kf=0.1, pf=0.5, out=None, ws=FAKE, wsb=
 
 def test_status_strings():
     L = _lib.lib()
-    for s in range(8):
+    for s in range(9):
         assert L.spa2_status_str(s) != b"unknown status"
-    assert L.spa2_status_str(8) == b"unknown status"
+    assert L.spa2_status_str(9) == b"unknown status"
     assert L.spa2_num_blocks(32760, 128) == 256 and L.spa2_num_blocks(75600, 64) == 1182
     assert L.spa2_num_blocks(0, 64) == 0
 
@@ -155,6 +155,25 @@ def test_workspace_checks():
     head = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 3
     assert L.spa2_bwd(C.byref(d), *head, FAKE, n.value - 1, None) == _lib.E_WORKSPACE
     assert L.spa2_bwd(C.byref(d), *head, None, n.value, None) == _lib.E_WORKSPACE
+
+
+def test_bwd_noalloc_validation():
+    """The no-allocation backward validates like spa2_bwd and rejects a problem whose row
+    term exceeds its built-in scratch with SPA2_E_SCRATCH, all before any HIP call."""
+    L = _lib.lib()
+    args = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 3 + [None]
+    # q k v o o_f32 lse dout m dq dk dv stream
+    assert L.spa2_bwd_noalloc(C.byref(good(D=96)), *args) == _lib.E_SHAPE
+    a = list(args)
+    a[2] = None
+    assert L.spa2_bwd_noalloc(C.byref(good()), *a) == _lib.E_NULL
+    a = list(args)
+    a[0] = ODD
+    assert L.spa2_bwd_noalloc(C.byref(good()), *a) == _lib.E_ALIGN
+    rows = _lib.NOALLOC_SCRATCH_BYTES // 4
+    big = good(B=1, H=rows // 65536 + 1, N=65536)
+    assert L.spa2_bwd_noalloc(C.byref(big), *args) == _lib.E_SCRATCH
+    assert L.spa2_bwd_noalloc(C.byref(good(B=2, H=rows // 65536, N=65536)), *args) == _lib.E_SCRATCH
 
 
 def test_bwd_workspace_bytes():
