@@ -202,13 +202,14 @@ def main():
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     if train:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        dvec = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        bws = spa2.bwd_workspace(q, bq, bkv)  # row term, then the dQ pass's mean keys
+        dvec = spa2.row_term(bws, q)
         # the unrounded O is an optional extra output for the backward's row term; the dQ
         # pass's shift correction makes the bf16 O enough at this shape (sampled dQ 0.21%
         # vs 0.20% relative L2), so the step writes it only with --o-f32
         o_f32 = torch.empty(q.shape, dtype=torch.float32, device="cuda") if args.o_f32 else None
     else:
-        dq = dk = dv = dvec = o_f32 = None
+        dq = dk = dv = bws = dvec = o_f32 = None
 
     def stage_mask():
         spa2.mask(q, k, kf, pf, bq, bkv, out=bm, workspace=mws)
@@ -217,7 +218,7 @@ def main():
         spa2.fwd(q, k, v, bm, out=(o, lse), o_f32=o_f32)
 
     def stage_dq():  # dQ and the row term rowsum(dO * O), which the dK/dV pass reads
-        spa2.bwd_dq_rowterm(q, k, v, o, lse, do, dvec, bm, dq, o_f32=o_f32)
+        spa2.bwd_dq_rowterm(q, k, v, o, lse, do, bws, bm, dq, o_f32=o_f32)
 
     def stage_dkdv():
         spa2.bwd_dkdv(q, k, v, lse, do, dvec, bm, dk, dv)
@@ -511,25 +512,28 @@ def check_parity(inp, w, gmask, o, lse, dq, dk, dv):
         qblocks = [0, tm // 3, tm - 1]
         kblocks = [1, tn // 2, tn - 1]
         o_ref, lse_ref = oracle.attn_fwd_head(q, k, v, m, bq, bkv, rows=qblocks)
-        qr = np.concatenate([np.arange(i * bq, min(N, (i + 1) * bq)) for i in qblocks])
-        cmp = [("O", on[0, h][qr], o_ref[qr])]
+        qsegs = [np.arange(i * bq, min(N, (i + 1) * bq)) for i in qblocks]
+        qr = np.concatenate(qsegs)
+        # every sampled block is held to the bar on its own (worst block reported)
+        cmp = [("O", on[0, h], o_ref, qsegs)]
         if train:
             do = inp.head_f64("do", 0, h)
             rows = sorted(set(qblocks) | {i for j in kblocks for i in np.flatnonzero(m[:, j])})
             dq_ref, dk_ref, dv_ref = oracle.attn_bwd_head(q, k, v, do, m, bq, bkv, rows=rows)
-            kr = np.concatenate([np.arange(j * bkv, min(N, (j + 1) * bkv)) for j in kblocks])
-            cmp += [("dQ", dqn[0, h][qr], dq_ref[qr]), ("dK", dkn[0, h][kr], dk_ref[kr]),
-                    ("dV", dvn[0, h][kr], dv_ref[kr])]
-        for name, got, ref in cmp:
-            e = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-            errs[name] = max(errs.get(name, 0.0), e)
+            ksegs = [np.arange(j * bkv, min(N, (j + 1) * bkv)) for j in kblocks]
+            cmp += [("dQ", dqn[0, h], dq_ref, qsegs), ("dK", dkn[0, h], dk_ref, ksegs),
+                    ("dV", dvn[0, h], dv_ref, ksegs)]
+        for name, got, ref, segs in cmp:
+            for sg in segs:
+                e = float(np.linalg.norm(got[sg] - ref[sg]) / np.linalg.norm(ref[sg]))
+                errs[name] = max(errs.get(name, 0.0), e)
         errs["LSE_abs"] = max(errs.get("LSE_abs", 0.0), float(np.abs(ln[0, h][qr] - lse_ref[qr]).max()))
     tol = 2e-2 if inp.dtype == "bf16" else 1e-4
     for name in ("O", "dQ", "dK", "dV"):
         if name in errs:
             assert errs[name] <= tol, f"{name} rel-L2 {errs[name]}"
     return {"mask_mismatch_outside_p_band": mism, "mask_p_band_flips": band,
-            "rel_l2_sampled": {k_: float(f"{v_:.3e}") for k_, v_ in errs.items()},
+            "rel_l2_worst_sampled_block": {k_: float(f"{v_:.3e}") for k_, v_ in errs.items()},
             "seconds": round(time.time() - t0, 1)}
 
 

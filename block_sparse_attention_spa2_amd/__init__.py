@@ -18,7 +18,8 @@ from ._lib import Spa2Error  # noqa: F401
 
 __all__ = ["BlockMask", "pool", "mask", "select", "mask_lists", "fwd", "bwd", "bwd_noalloc",
            "bwd_prep", "bwd_dkdv", "bwd_dq", "bwd_dq_rowterm", "error_terms",
-           "mask_workspace_size", "bwd_workspace_size", "num_blocks", "Spa2Error"]
+           "mask_workspace_size", "bwd_workspace_size", "bwd_workspace", "row_term", "num_blocks",
+           "Spa2Error"]
 
 
 def num_blocks(n: int, b: int) -> int:
@@ -122,6 +123,26 @@ def bwd_workspace_size(q: torch.Tensor, bq: int = 128, bkv: int = 64) -> int:
     _lib.check("spa2_bwd_workspace_size",
                _lib.lib().spa2_bwd_workspace_size(C.byref(_desc(q, bq, bkv)), C.byref(n)))
     return int(n.value)
+
+
+def bwd_workspace(q: torch.Tensor, bq: int = 128, bkv: int = 64) -> torch.Tensor:
+    """A backward workspace (uint8, bwd_workspace_size bytes) on q's device."""
+    return torch.empty(bwd_workspace_size(q, bq, bkv), dtype=torch.uint8, device=q.device)
+
+
+def row_term(workspace: torch.Tensor, q: torch.Tensor) -> torch.Tensor:
+    """The row term rowsum(dO * O) held at the start of a backward workspace: a float32
+    [B, H, N] view of its first B*H*N*4 bytes."""
+    B, H, N = q.shape[:3]
+    if workspace.dtype != torch.uint8 or workspace.numel() < B * H * N * 4:
+        raise ValueError("workspace: too small for the row term (uint8)")
+    return workspace[:B * H * N * 4].view(torch.float32).view(B, H, N)
+
+
+def _expect_ws(workspace: torch.Tensor, q: torch.Tensor, bq: int, bkv: int) -> None:
+    need = bwd_workspace_size(q, bq, bkv)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need or workspace.device != q.device:
+        raise ValueError(f"workspace: need {need} bytes (uint8) on {q.device}")
 
 
 def pool(q: torch.Tensor, k: torch.Tensor, bq: int = 128, bkv: int = 64):
@@ -283,7 +304,8 @@ def bwd_prep(o: torch.Tensor, do: torch.Tensor, dvec: torch.Tensor, bq: int = 12
 
 
 def bwd_dkdv(q, k, v, lse, do, dvec, bm: BlockMask | None, dk, dv, bq: int = 128, bkv: int = 64):
-    """dK, dV pass of bwd (second kernel)."""
+    """dK, dV pass of bwd, reading the row term dvec (float32 [B, H, N], e.g.
+    row_term(workspace, q))."""
     if bm is not None:
         bq, bkv = bm.bq, bm.bkv
         _check_bm(bm, q)
@@ -298,26 +320,29 @@ def bwd_dkdv(q, k, v, lse, do, dvec, bm: BlockMask | None, dk, dv, bq: int = 128
     return dk, dv
 
 
-def bwd_dq(q, k, v, lse, do, dvec, bm: BlockMask | None, dq, bq: int = 128, bkv: int = 64):
-    """dQ pass of bwd (third kernel)."""
+def bwd_dq(q, k, v, lse, do, workspace, bm: BlockMask | None, dq, bq: int = 128,
+           bkv: int = 64):
+    """dQ pass of bwd, reading the row term from the start of `workspace` (a backward
+    workspace, see bwd_workspace / row_term); it writes the workspace's mean keys."""
     if bm is not None:
         bq, bkv = bm.bq, bm.bkv
         _check_bm(bm, q)
     for name, t in (("k", k), ("v", v), ("do", do), ("dq", dq)):
         _expect(name, t, q.shape, q.dtype)
     _expect("lse", lse, q.shape[:3], torch.float32)
-    _expect("dvec", dvec, q.shape[:3], torch.float32)
+    _expect_ws(workspace, q, bq, bkv)
     bmc = C.byref(bm.c()) if bm is not None else None
     _lib.check("spa2_bwd_dq", _lib.lib().spa2_bwd_dq(
-        C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dvec),
-        bmc, _ptr(dq), _stream(q)))
+        C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do),
+        _ptr(workspace), workspace.numel(), bmc, _ptr(dq), _stream(q)))
     return dq
 
 
-def bwd_dq_rowterm(q, k, v, o, lse, do, dvec, bm: BlockMask | None, dq, bq: int = 128,
+def bwd_dq_rowterm(q, k, v, o, lse, do, workspace, bm: BlockMask | None, dq, bq: int = 128,
                    bkv: int = 64, *, o_f32: torch.Tensor | None = None):
-    """dQ pass that also writes the row term dvec = rowsum(dO * O) (O = o_f32 if given);
-    bwd runs it before the dK/dV pass, which reads dvec."""
+    """dQ pass that also writes the row term rowsum(dO * O) (O = o_f32 if given) at the
+    start of `workspace` (row_term(workspace, q) views it); bwd runs it before the dK/dV
+    pass, which reads the row term."""
     if bm is not None:
         bq, bkv = bm.bq, bm.bkv
         _check_bm(bm, q)
@@ -326,11 +351,11 @@ def bwd_dq_rowterm(q, k, v, o, lse, do, dvec, bm: BlockMask | None, dq, bq: int 
     if o_f32 is not None:
         _expect("o_f32", o_f32, q.shape, torch.float32)
     _expect("lse", lse, q.shape[:3], torch.float32)
-    _expect("dvec", dvec, q.shape[:3], torch.float32)
+    _expect_ws(workspace, q, bq, bkv)
     bmc = C.byref(bm.c()) if bm is not None else None
     _lib.check("spa2_bwd_dq_rowterm", _lib.lib().spa2_bwd_dq_rowterm(
         C.byref(_desc(q, bq, bkv)), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_f32), _ptr(lse),
-        _ptr(do), bmc, _ptr(dvec), _ptr(dq), _stream(q)))
+        _ptr(do), bmc, _ptr(workspace), workspace.numel(), _ptr(dq), _stream(q)))
     return dq
 
 

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libspa2.so")
 
 OK, E_NULL, E_SHAPE, E_DTYPE, E_PARAM, E_WORKSPACE, E_HIP, E_ALIGN, E_SCRATCH = range(9)
-NOALLOC_SCRATCH_BYTES = 16 << 20  # SPA2_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SPA2_NOALLOC_SCRATCH_BYTES
 F32, BF16 = 0, 1
 
 
@@ -43,9 +43,9 @@ SIGNATURES = {
     "spa2_bwd_noalloc": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P, _P]),
     "spa2_bwd_prep": (C.c_int, [_DESC, _P, _P, _P, _P, _P]),
     "spa2_bwd_dkdv": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P]),
-    "spa2_bwd_dq": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _BM, _P, _P]),
+    "spa2_bwd_dq": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _BM, _P, _P]),
     "spa2_error_terms": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P]),
-    "spa2_bwd_dq_rowterm": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P, _BM, _P, _P, _P]),
+    "spa2_bwd_dq_rowterm": (C.c_int, [_DESC, _P, _P, _P, _P, _P, _P, _P, _BM, _P, _SZ, _P, _P]),
 }
 
 _lib = None

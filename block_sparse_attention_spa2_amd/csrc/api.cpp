@@ -11,8 +11,8 @@
 #include "../../include/spa2.h"
 #include "kernels.h"
 
-// Scratch memory of spa2_bwd_noalloc (the backward's row term, float per query row), for
-// callers that cannot allocate. Every GPU the library runs on holds its own copy until the
+// Scratch memory of spa2_bwd_noalloc (the backward's workspace: row term and mean keys),
+// for callers that cannot allocate. Every GPU the library runs on holds its own copy until the
 // process ends. In host code `scratch` is only a stand-in for the symbol: its device
 // address comes from hipGetSymbolAddress (scratch_on_device below).
 static __device__ __align__(256) unsigned char scratch[SPA2_NOALLOC_SCRATCH_BYTES];
@@ -89,6 +89,17 @@ constexpr size_t kWsAlign = 256;
 size_t mask_ws_bytes(const spa2::Shape& s) {
   const size_t bh = (size_t)s.BH(), pitch = (size_t)spa2::kPoolPitch(s.D);
   return bh * ((size_t)(s.Tm + s.Tn) * pitch + (size_t)s.Tm * s.Tn) * sizeof(double) + kWsAlign;
+}
+
+// The backward workspace holds the row term (float per query row) from its start, then,
+// for bf16, the mean key of every key tile from the first 256-byte boundary after it.
+size_t bwd_ws_bytes(const spa2::Shape& s) {
+  const size_t kmean = spa2::bwd_kmean_bytes(s);
+  return (size_t)s.BH() * s.N * sizeof(float) + (kmean ? kWsAlign + kmean : 0);
+}
+void* bwd_kmean(void* ws, const spa2::Shape& s) {
+  const uintptr_t end = (uintptr_t)ws + (size_t)s.BH() * s.N * sizeof(float);
+  return (void*)((end + kWsAlign - 1) & ~(uintptr_t)(kWsAlign - 1));
 }
 
 spa2_status hip_status(const char* where, hipError_t e) {
@@ -264,7 +275,7 @@ spa2_status spa2_bwd_workspace_size(const spa2_desc* desc, size_t* bytes) {
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
   if (!bytes) return SPA2_E_NULL;
-  *bytes = (size_t)s.BH() * s.N * sizeof(float);
+  *bytes = bwd_ws_bytes(s);
   return SPA2_OK;
 }
 
@@ -282,13 +293,13 @@ spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const 
   if (st != SPA2_OK) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
-  if (!workspace || ws_bytes < (size_t)s.BH() * s.N * sizeof(float)) return SPA2_E_WORKSPACE;
+  if (!workspace || ws_bytes < bwd_ws_bytes(s)) return SPA2_E_WORKSPACE;
   if (!aligned16({q, k, v, o, o_f32, dout, dq, dk, dv}) || !aligned4({lse, workspace}) ||
       !lists_aligned(m))
     return SPA2_E_ALIGN;
   return hip_status("bwd", spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, dk, dv,
-                                            (float*)workspace, spa2::kBwdDqRow | spa2::kBwdDkdv,
-                                            (hipStream_t)stream));
+                                            (float*)workspace, bwd_kmean(workspace, s),
+                                            spa2::kBwdDqRow | spa2::kBwdDkdv, (hipStream_t)stream));
 }
 
 spa2_status spa2_bwd_noalloc(const spa2_desc* desc, const void* q, const void* k, const void* v,
@@ -302,28 +313,33 @@ spa2_status spa2_bwd_noalloc(const spa2_desc* desc, const void* q, const void* k
   if (m && (!m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)) return SPA2_E_NULL;
   if (!aligned16({q, k, v, o, o_f32, dout, dq, dk, dv}) || !aligned4({lse}) || !lists_aligned(m))
     return SPA2_E_ALIGN;
-  if ((size_t)s.BH() * s.N * sizeof(float) > (size_t)SPA2_NOALLOC_SCRATCH_BYTES) return SPA2_E_SCRATCH;
+  if (bwd_ws_bytes(s) > (size_t)SPA2_NOALLOC_SCRATCH_BYTES) return SPA2_E_SCRATCH;
   const hipStream_t hs = (hipStream_t)stream;
   void* ws = nullptr;
   if ((st = scratch_on_device(hs, &ws)) != SPA2_OK) return st;
   return hip_status("bwd_noalloc", spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, dk, dv,
-                                                    (float*)ws, spa2::kBwdDqRow | spa2::kBwdDkdv, hs));
+                                                    (float*)ws, bwd_kmean(ws, s),
+                                                    spa2::kBwdDqRow | spa2::kBwdDkdv, hs));
 }
 
 spa2_status spa2_bwd_dq_rowterm(const spa2_desc* desc, const void* q, const void* k,
                                 const void* v, const void* o, const float* o_f32,
                                 const float* lse, const void* dout,
-                                const spa2_blockmask* m, float* dvec, void* dq, void* stream) {
+                                const spa2_blockmask* m, void* workspace, size_t ws_bytes,
+                                void* dq, void* stream) {
   spa2::Shape s;
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dvec || !dq) return SPA2_E_NULL;
+  if (!q || !k || !v || !o || !lse || !dout || !dq) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
-  if (!aligned16({q, k, v, o, o_f32, dout, dq}) || !aligned4({lse, dvec}) || !lists_aligned(m))
+  if (!workspace || ws_bytes < bwd_ws_bytes(s)) return SPA2_E_WORKSPACE;
+  if (!aligned16({q, k, v, o, o_f32, dout, dq}) || !aligned4({lse, workspace}) ||
+      !lists_aligned(m))
     return SPA2_E_ALIGN;
   return hip_status("bwd_dq_rowterm",
                     spa2::launch_bwd(s, q, k, v, o, o_f32, lse, dout, m, dq, nullptr, nullptr,
-                                     dvec, spa2::kBwdDqRow, (hipStream_t)stream));
+                                     (float*)workspace, bwd_kmean(workspace, s), spa2::kBwdDqRow,
+                                     (hipStream_t)stream));
 }
 
 spa2_status spa2_error_terms(const spa2_desc* desc, const float* o_sparse, const float* lse_sparse,
@@ -350,7 +366,7 @@ spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f
   if (!aligned16({o, o_f32, dout}) || !aligned(dvec, 4)) return SPA2_E_ALIGN;
   return hip_status("bwd_prep", spa2::launch_bwd(s, nullptr, nullptr, nullptr, o, o_f32, nullptr, dout,
                                                  nullptr, nullptr, nullptr, nullptr, dvec,
-                                                 spa2::kBwdPrep, (hipStream_t)stream));
+                                                 nullptr, spa2::kBwdPrep, (hipStream_t)stream));
 }
 
 spa2_status spa2_bwd_dkdv(const spa2_desc* desc, const void* q, const void* k, const void* v,
@@ -364,23 +380,24 @@ spa2_status spa2_bwd_dkdv(const spa2_desc* desc, const void* q, const void* k, c
   if (!aligned16({q, k, v, dout, dk, dv}) || !aligned4({lse, dvec}) || !lists_aligned(m))
     return SPA2_E_ALIGN;
   return hip_status("bwd_dkdv", spa2::launch_bwd(s, q, k, v, nullptr, nullptr, lse, dout, m, nullptr, dk,
-                                                 dv, (float*)dvec, spa2::kBwdDkdv,
+                                                 dv, (float*)dvec, nullptr, spa2::kBwdDkdv,
                                                  (hipStream_t)stream));
 }
 
 spa2_status spa2_bwd_dq(const spa2_desc* desc, const void* q, const void* k, const void* v,
-                        const float* lse, const void* dout, const float* dvec,
+                        const float* lse, const void* dout, void* workspace, size_t ws_bytes,
                         const spa2_blockmask* m, void* dq, void* stream) {
   spa2::Shape s;
   spa2_status st = check_desc(desc, &s);
   if (st != SPA2_OK) return st;
-  if (!q || !k || !v || !lse || !dout || !dvec || !dq) return SPA2_E_NULL;
+  if (!q || !k || !v || !lse || !dout || !dq) return SPA2_E_NULL;
   if (m && (!m->row_cnt || !m->row_idx)) return SPA2_E_NULL;
-  if (!aligned16({q, k, v, dout, dq}) || !aligned4({lse, dvec}) || !lists_aligned(m))
+  if (!workspace || ws_bytes < bwd_ws_bytes(s)) return SPA2_E_WORKSPACE;
+  if (!aligned16({q, k, v, dout, dq}) || !aligned4({lse, workspace}) || !lists_aligned(m))
     return SPA2_E_ALIGN;
   return hip_status("bwd_dq", spa2::launch_bwd(s, q, k, v, nullptr, nullptr, lse, dout, m, dq, nullptr,
-                                               nullptr, (float*)dvec, spa2::kBwdDq,
-                                               (hipStream_t)stream));
+                                               nullptr, (float*)workspace, bwd_kmean(workspace, s),
+                                               spa2::kBwdDq, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -45,6 +45,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;
+  const bf16* kmean;  // bf16 dQ pass: mean key of every key tile [BH, tiles, D]
   int N, Tm, Tn, BH;
   int bq_block, bkv_block;  // rows / keys of a mask block (multiples of the kernels' tiles)
   int qsub, ksub;           // log2 of the query tiles per block and key tiles per key block
@@ -86,6 +87,40 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// Mean key of every key tile of BKVT keys (the last tile over its valid keys), fp32
+// sums rounded once to bf16: the reference vectors of the bf16 dQ pass's corrections,
+// formed once per call instead of in every query block that keeps the tile.
+// One workgroup per (head, tile); TPR threads per row move 16-byte chunks.
+// ------------------------------------------------------------------------------------
+template <int D, int BKVT>
+__global__ __launch_bounds__(256) void kmean_kernel(const bf16* __restrict__ k, bf16* __restrict__ out,
+                                                    int N, int tiles) {
+  constexpr int TPR = D / 8;    // threads per row
+  constexpr int RP = 256 / TPR; // rows in flight
+  __shared__ float red[RP][D];
+  const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int lo = tile * BKVT, hi = min(N, lo + BKVT);
+  const bf16* base = k + (size_t)bh * N * D;
+  const int c = threadIdx.x % TPR, r0 = threadIdx.x / TPR;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r = lo + r0; r < hi; r += RP) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(base + (size_t)r * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (float)x[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[r0][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float sum = 0.f;
+    for (int r = 0; r < RP; ++r) sum += red[r][threadIdx.x];
+    out[((size_t)bh * tiles + tile) * D + threadIdx.x] = (bf16)(hi > lo ? sum / (float)(hi - lo) : 0.f);
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // dQ: per query block, over its kept key blocks.
 //   S^T = K Q^T, dP^T = V dO^T (A = K, V rows from LDS; B = Q, dO in registers),
 //   dS^T = P^T * (dP^T - Dv), dQ^T += K^T dS^T (A = K^T via transpose reads).
@@ -102,9 +137,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // What remains involves only K_k - c_j, so c_j is the block's mean key: it removes the
 // shared part whatever its shape (a first-key reference also carries that key's own
 // noise, which on keys with a smooth positional component left more error than no
-// correction at all). The mean comes from the matrix unit: each wave multiplies the K^T
-// fragments it reads for the dQ product by a constant 1/BKV operand for its share of the
-// head dimensions. Both terms are rank-one updates per block, w_j (x) c_j with
+// correction at all). The means come from kmean_kernel, once per call; wave 0 reads the
+// next block's mean with the tile loads and copies it into LDS after the next barrier.
+// Both terms are rank-one updates per block, w_j (x) c_j with
 // w_j = sum_k r_k or P^blk_j. They are batched on the matrix unit, eight blocks at a
 // time: each lane group g (16 lanes, a quarter of the block's keys) keeps its partial
 // weights of the last eight blocks as the eight reduction slots 8g .. 8g + 7 of an MFMA
@@ -126,7 +161,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   using KV = Tile<T, BKV, D>;
   constexpr bool kCorr = sizeof(T) == 2;
   using CM = Tile<T, 32, D>;  // c_j of one batch of eight blocks, four copies (bf16 only)
-  constexpr int MD = (DT + NW - 1) / NW;  // mean-key output tiles per wave
   // K/V stages in separate LDS variables, named statically (see the forward kernel). The
   // code also runs three stages (loads issued two blocks ahead, partial vmcnt waits), which
   // measured slower than two with eight waves per workgroup.
@@ -168,6 +202,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
   };
   if (cnt > 0) issue(stage0, block_at(0, 0));
   if (NS == 3 && cnt > 1) issue(stage1, block_at(0, 1));
+  // mean key rows: lane c of each 16-lane group of wave 0 holds 16-byte chunk c of the
+  // mean of the block whose C row is written next (read one block ahead, with the tiles)
+  static_assert(!kCorr || CM::kChunks <= 16, "a bf16 key row is at most 16 chunks");
+  const bf16* KM = kCorr ? a.kmean + (size_t)bh * ((size_t)a.Tn << a.ksub) * D : nullptr;
+  const int mc = l & 15;
+  u32x4 mrow{0u, 0u, 0u, 0u};
+  auto load_mean = [&](int j) {
+    if (kCorr && w == 0 && mc < CM::kChunks)
+      mrow = *reinterpret_cast<const u32x4*>(KM + (size_t)j * D + mc * 8);
+  };
+  if (cnt > 0) load_mean(block_at(0, 0));
   if constexpr (kCorr) {  // C starts at zero: unfilled rows meet zero weights
     const u32x4 z{0u, 0u, 0u, 0u};
     for (int o = tid * 16; o < CM::kBytes; o += 64 * NW * 16) {
@@ -247,11 +292,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
   }
-  // B operand of 1/BKV (a power of two, exact in bf16): K^T times it is the block's mean
-  // key in every column
-  F inv_bkv;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) inv_bkv[e] = (T)(1.0f / BKV);
 
   auto shift_in = [&](u32x4& r, float x) {  // drop element 0, append bf16(x) as element 7
     const unsigned b = __builtin_bit_cast(unsigned short, (bf16)x);
@@ -292,13 +332,23 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     const int j = block_at(t, 0);
     const int ahead = t + NS - 1;
     const int jn = block_at(t, NS - 1);
+    const int jm = NS == 2 ? jn : block_at(t, 1);  // the next block, for its mean key
     if (!dense) bq.advance(t);
     // this wave's loads of block t have landed: with three stages the loads of block
     // t + 1 (issued later; loads complete in order) may still be in flight
     if (NS == 3 && t + 1 < cnt) wait_vmem_below<kBlockLoads>();
     else wait_vmem();
     lds_barrier();  // ... and every other wave's; block t-1 is no longer being read
+    if constexpr (kCorr) {
+      // this block's mean key (loaded during the previous block), four copies (one per
+      // lane group of wave 0): rows 4 g' + i (i = t mod 8 < 4) or 16 + 4 g' + (i - 4)
+      if (w == 0 && mc < CM::kChunks) {
+        const int i = t & 7;
+        CM::store_chunk(((t >> 3) & 1) ? cm1 : cm0, (i < 4 ? i : 12 + i) + 4 * (l >> 4), mc, mrow);
+      }
+    }
     if (ahead < cnt) issue(next, jn);
+    if (t + 1 < cnt) load_mean(jm);
     const char* Kb = stage;
     const char* Vb = stage + KV::kBytes;
     if constexpr (kCorr) {
@@ -360,11 +410,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
     f32x4 cs[QT];  // element g: sum of bf16(dS_k) over this lane group's keys
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) cs[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // the block's mean key for this wave's share of the head dimensions (output tiles
-    // dt = w, w + NW, ...): lane holds mean[16 dt + 4 g + e] (every column the same)
-    f32x4 cmean[MD];
-#pragma unroll
-    for (int md = 0; md < MD; ++md) cmean[md] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < UPV; ++u) {
       F pf[QT];
@@ -380,24 +425,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
         KV::read_col4(Kb, 32 * u + 16, dt * 16, kt_, 1);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = E::mma(kt_, pf[qt], acc[dt][qt]);
-        if (kCorr && dt % NW == w) cmean[dt / NW] = E::mma(kt_, inv_bkv, cmean[dt / NW]);
-      }
-    }
-    if constexpr (kCorr) {
-      // C rows of block i = t mod 8: rows 4 g' + i (i < 4) or 16 + 4 g' + (i - 4) for the
-      // four copies g' = 0..3, written by lanes 0..3 (lane g' writes copy g'); visible to
-      // every wave after the next block's barrier, before the batch's flush reads them
-      if (c16 < 4) {
-        const int i = t & 7;
-        const int row = (i < 4 ? i : 12 + i) + 4 * c16;
-        char* cmw = ((t >> 3) & 1) ? cm1 : cm0;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const int dt = md * NW + w;
-          if (dt < DT)
-            *reinterpret_cast<bf16x4*>(cmw + CM::offset(row, dt * 16 + 4 * g)) =
-                bf16x4{(bf16)cmean[md][0], (bf16)cmean[md][1], (bf16)cmean[md][2], (bf16)cmean[md][3]};
-        }
       }
     }
     if constexpr (kCorr) {
@@ -749,23 +776,27 @@ constexpr int dq_waves() {
 
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* o_f32, const float* lse, const void* dout, const spa2_blockmask* m, void* dq,
-                      void* dk, void* dv, float* dvec, int stages, hipStream_t st) {
+                      void* dk, void* dv, float* dvec, void* kmean, int stages, hipStream_t st) {
   BwdArgs a{q, k, v, o, o_f32, lse, dout,
             m ? m->row_cnt : nullptr, m ? m->row_idx : nullptr,
             m ? m->col_cnt : nullptr, m ? m->col_idx : nullptr,
             m ? m->row_order : nullptr, m ? m->col_order : nullptr,
-            dq, dk, dv, dvec, s.N, s.Tm, s.Tn, s.BH(), s.BQ, s.BKV, s.qsub(), s.ksub(), 0,
+            dq, dk, dv, dvec, (const bf16*)kmean, s.N, s.Tm, s.Tn, s.BH(), s.BQ, s.BKV, s.qsub(), s.ksub(), 0,
             (float)(1.4426950408889634 / sqrt((double)s.D)), (float)(1.0 / sqrt((double)s.D))};
   const int tpr = s.D * (s.dtype == SPA2_BF16 ? 2 : 4) / 16;
   const int rpb = 256 / tpr;
   const size_t rows = (size_t)s.BH() * s.N;
   const dim3 gpre((unsigned)((rows + rpb - 1) / rpb));
   const dim3 gq((s.BH() * s.Tm) << s.qsub()), gk((s.BH() * s.Tn) << s.ksub());
+  const int tiles = bwd_key_tiles(s);
 #define SPA2_BWD(T, D, BQ, BK)                                                       \
   do {                                                                               \
     constexpr int nq = dq_waves<T, D, BQ, BK>();                                     \
     auto launch_dq = [&](auto nqt) {                                                 \
       constexpr int NQ = decltype(nqt)::value;                                       \
+      if constexpr (sizeof(T) == 2)                                                  \
+        kmean_kernel<D, BK><<<dim3((unsigned)(s.BH() * tiles)), 256, 0, st>>>(       \
+            (const bf16*)k, (bf16*)kmean, s.N, tiles);                                \
       if (!m) bwd_dq_kernel<T, D, BQ, BK, 0, true, NQ><<<gq, 64 * NQ, 0, st>>>(a);  \
       else if (s.ksub()) bwd_dq_kernel<T, D, BQ, BK, 1, false, NQ><<<gq, 64 * NQ, 0, st>>>(a); \
       else bwd_dq_kernel<T, D, BQ, BK, 0, false, NQ><<<gq, 64 * NQ, 0, st>>>(a);    \

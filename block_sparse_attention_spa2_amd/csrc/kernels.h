@@ -61,8 +61,16 @@ hipError_t launch_error_terms(const Shape& s, const float* os, const float* ls, 
 // kBwdDqRow: the dQ pass that also computes the row term (instead of kBwdPrep), run
 // before the dK/dV pass.
 constexpr int kBwdPrep = 1, kBwdDkdv = 2, kBwdDq = 4, kBwdDqRow = 8, kBwdAll = 7;
+// Key tiles of the dQ pass per head (the bf16 pass keeps one mean key per tile).
+inline int bwd_key_tiles(const Shape& s) { return s.Tn << s.ksub(); }
+// Bytes of the per-tile mean keys (bf16 [B*H, key tiles, D]); none for fp32.
+inline size_t bwd_kmean_bytes(const Shape& s) {
+  return s.dtype == SPA2_BF16 ? (size_t)s.BH() * bwd_key_tiles(s) * s.D * 2 : 0;
+}
+// dvec: the row term, float [B*H*N]; kmean: bwd_kmean_bytes, 16-byte aligned (the dQ
+// stages of a bf16 backward write it first, then read it)
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* o_f32, const float* lse, const void* dout, const spa2_blockmask* m, void* dq,
-                      void* dk, void* dv, float* dvec, int stages, hipStream_t st);
+                      void* dk, void* dv, float* dvec, void* kmean, int stages, hipStream_t st);
 
 }  // namespace spa2

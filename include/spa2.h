@@ -156,13 +156,17 @@ spa2_status spa2_fwd(const spa2_desc* desc, const void* q, const void* k, const 
                      const spa2_blockmask* m, void* o, float* lse, float* o_f32,
                      void* stream);
 
-/* Workspace bytes that spa2_bwd needs (the per-row dot(dO, O) vector, float). */
+/* Workspace bytes that spa2_bwd needs. The workspace holds, from its start, the row term
+ * rowsum(dO * O) (float [B, H, N]; the dQ pass stores it, the dK/dV pass reads it) and, for
+ * bf16, the mean key of every key tile of the dQ pass (bf16 [B, H, tiles, D], from the
+ * first 256-byte boundary after the row term; tiles = 2 T_n for b_kv = 128, else T_n),
+ * formed at the start of each dQ pass as the reference vectors of its rounding
+ * corrections: B H N 4 bytes for fp32, B H N 4 + 256 + B H tiles D 2 for bf16. */
 spa2_status spa2_bwd_workspace_size(const spa2_desc* desc, size_t* bytes);
 
-/* The same size as a plain return value: B * H * N * 4 bytes for a valid descriptor, 0 for
- * an invalid one (or NULL), which spa2_bwd then rejects with its own status. The backward
- * is deterministic and always needs this buffer: its dK/dV pass reads the row term
- * rowsum(dO * O) that the dQ pass stores there. */
+/* The same size as a plain return value, 0 for an invalid descriptor (or NULL), which
+ * spa2_bwd then rejects with its own status. The backward is deterministic and always
+ * needs this buffer. */
 size_t spa2_bwd_workspace_bytes(const spa2_desc* desc);
 
 /* Backward of spa2_fwd with the same mask held fixed (the mask gets no gradient):
@@ -177,18 +181,19 @@ spa2_status spa2_bwd(const spa2_desc* desc, const void* q, const void* k, const 
                      const spa2_blockmask* m, void* dq, void* dk, void* dv, void* workspace,
                      size_t ws_bytes, void* stream);
 
-/* Bytes of device scratch that spa2_bwd_noalloc holds per GPU: the row term of up to
- * 4,194,304 query rows (B * H * N), e.g. 40 heads of 75,600 tokens. */
-#define SPA2_NOALLOC_SCRATCH_BYTES (16u << 20)
+/* Bytes of device scratch that spa2_bwd_noalloc holds per GPU: the backward workspace of
+ * up to this size (spa2_bwd_workspace_bytes), e.g. 40 heads of 75,600 tokens at D = 128
+ * with 64-key blocks (24.2 MB). */
+#define SPA2_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* spa2_bwd without a workspace argument, for callers that cannot allocate device memory
  * (code under graph capture, tight serving loops, harnesses that forbid allocation). The
- * row term goes to a scratch array built into the library (SPA2_NOALLOC_SCRATCH_BYTES per
+ * workspace is a scratch array built into the library (SPA2_NOALLOC_SCRATCH_BYTES per
  * GPU, held until the process ends); the call itself allocates nothing. Same arguments,
  * kernels and results as spa2_bwd (bit for bit). Returns SPA2_E_SCRATCH, before any HIP
- * call, when B * H * N * 4 bytes exceed the scratch. The scratch is shared by every call on
- * a GPU and keeps the last call's contents (nothing in it needs clearing: the dQ pass
- * writes every row term before the dK/dV pass reads it), so calls that overlap on one GPU
+ * call, when spa2_bwd_workspace_bytes exceeds the scratch. The scratch is shared by every
+ * call on a GPU and keeps the last call's contents (nothing in it needs clearing: the dQ
+ * pass writes every mean key and row term before they are read), so calls that overlap on one GPU
  * (other streams, other threads) race: serialise them. The first call on a device looks
  * up the scratch address there (hipGetSymbolAddress on the stream's device). */
 spa2_status spa2_bwd_noalloc(const spa2_desc* desc, const void* q, const void* k, const void* v,
@@ -200,24 +205,27 @@ spa2_status spa2_bwd_noalloc(const spa2_desc* desc, const void* q, const void* k
  * dK/dV pass on another stream). spa2_bwd is exactly spa2_bwd_dq_rowterm, then
  * spa2_bwd_dkdv, on one stream.
  *   spa2_bwd_dq_rowterm: dQ from the row lists (one workgroup per query block), and the
- *                  row term dvec[B, H, N] (float, device) = rowsum(dO * O), O = o_f32 if
- *                  given, computed by the same pass from the dO rows it loads anyway;
+ *                  row term rowsum(dO * O), O = o_f32 if given, computed by the same pass
+ *                  from the dO rows it loads anyway, stored at the workspace's start;
  *   spa2_bwd_dkdv: dK, dV from the column lists (one workgroup per key block);
  *   spa2_bwd_prep: the row term alone (a separate pass over O and dO);
- *   spa2_bwd_dq:   dQ alone, reading dvec.
- * dvec must hold the row term for the same O and dO (from either pass; the two sum in
+ *   spa2_bwd_dq:   dQ alone, reading the row term from the workspace's start.
+ * workspace / ws_bytes: as for spa2_bwd (the dQ passes write its mean keys); dvec: the row
+ * term, float [B, H, N] (device), normally the first B H N floats of that workspace.
+ * The row term must be for the same O and dO (from either pass; the two sum in
  * different orders, so results agree to rounding, not bit for bit). */
 spa2_status spa2_bwd_dq_rowterm(const spa2_desc* desc, const void* q, const void* k,
                                 const void* v, const void* o, const float* o_f32,
                                 const float* lse, const void* dout,
-                                const spa2_blockmask* m, float* dvec, void* dq, void* stream);
+                                const spa2_blockmask* m, void* workspace, size_t ws_bytes,
+                                void* dq, void* stream);
 spa2_status spa2_bwd_prep(const spa2_desc* desc, const void* o, const float* o_f32,
                           const void* dout, float* dvec, void* stream);
 spa2_status spa2_bwd_dkdv(const spa2_desc* desc, const void* q, const void* k, const void* v,
                           const float* lse, const void* dout, const float* dvec,
                           const spa2_blockmask* m, void* dk, void* dv, void* stream);
 spa2_status spa2_bwd_dq(const spa2_desc* desc, const void* q, const void* k, const void* v,
-                        const float* lse, const void* dout, const float* dvec,
+                        const float* lse, const void* dout, void* workspace, size_t ws_bytes,
                         const spa2_blockmask* m, void* dq, void* stream);
 
 /* Error decomposition of the sparse output against the dense one (rainbus summary,

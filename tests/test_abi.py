@@ -78,9 +78,9 @@ def test_bad_desc(kw, code):
                       FAKE, FAKE, 1 << 40, None) == code
     assert L.spa2_bwd_prep(C.byref(d), FAKE, None, FAKE, FAKE, None) == code
     assert L.spa2_bwd_dkdv(C.byref(d), *[FAKE] * 6, None, FAKE, FAKE, None) == code
-    assert L.spa2_bwd_dq(C.byref(d), *[FAKE] * 6, None, FAKE, None) == code
-    assert L.spa2_bwd_dq_rowterm(C.byref(d), *[FAKE] * 4, None, FAKE, FAKE, None, FAKE, FAKE,
-                                 None) == code
+    assert L.spa2_bwd_dq(C.byref(d), *[FAKE] * 6, 1 << 40, None, FAKE, None) == code
+    assert L.spa2_bwd_dq_rowterm(C.byref(d), *[FAKE] * 4, None, FAKE, FAKE, None, FAKE, 1 << 40,
+                                 FAKE, None) == code
     n = C.c_size_t(0)
     assert L.spa2_mask_workspace_size(C.byref(d), C.byref(n)) == code
 
@@ -119,18 +119,20 @@ def test_null_pointers():
     # the staged backward: prep (o, o_f32, dout, dvec), dkdv, dq
     assert L.spa2_bwd_prep(d, FAKE, None, None, FAKE, None) == _lib.E_NULL
     assert L.spa2_bwd_prep(d, FAKE, None, FAKE, None, None) == _lib.E_NULL
-    st = [FAKE] * 6  # q k v lse dout dvec
+    st = [FAKE] * 6  # q k v lse dout dvec (dkdv) / workspace (dq)
     for i in range(6):
         a = list(st)
         a[i] = None
         assert L.spa2_bwd_dkdv(d, *a, None, FAKE, FAKE, None) == _lib.E_NULL
-        assert L.spa2_bwd_dq(d, *a, None, FAKE, None) == _lib.E_NULL
+        # a missing workspace is a workspace error, like spa2_bwd's
+        want = _lib.E_WORKSPACE if i == 5 else _lib.E_NULL
+        assert L.spa2_bwd_dq(d, *a, 1 << 40, None, FAKE, None) == want, i
     assert L.spa2_bwd_dkdv(d, *st, C.byref(bm(col_idx=None)), FAKE, FAKE, None) == _lib.E_NULL
-    assert L.spa2_bwd_dq(d, *st, C.byref(bm(row_cnt=None)), FAKE, None) == _lib.E_NULL
-    assert L.spa2_bwd_dq(d, *st, None, None, None) == _lib.E_NULL
-    # dQ with the row term: q k v o o_f32 lse dout m dvec dq stream
-    rargs = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 2 + [None]
-    for i in (0, 1, 2, 3, 5, 6, 8, 9):
+    assert L.spa2_bwd_dq(d, *st, 1 << 40, C.byref(bm(row_cnt=None)), FAKE, None) == _lib.E_NULL
+    assert L.spa2_bwd_dq(d, *st, 1 << 40, None, None, None) == _lib.E_NULL
+    # dQ with the row term: q k v o o_f32 lse dout m ws ws_bytes dq stream
+    rargs = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE, 1 << 40, FAKE, None]
+    for i in (0, 1, 2, 3, 5, 6, 10):
         a = list(rargs)
         a[i] = None
         assert L.spa2_bwd_dq_rowterm(d, *a) == _lib.E_NULL, i
@@ -151,10 +153,22 @@ def test_workspace_checks():
     assert mask_call(ws=None) == _lib.E_WORKSPACE
     assert mask_call(wsb=n.value - 1) == _lib.E_WORKSPACE
     assert L.spa2_bwd_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
-    assert n.value == 2 * 1000 * 4
+    # bf16: the row term, 256 bytes of alignment slack, a bf16 mean key per 64-key tile
+    assert n.value == 2 * 1000 * 4 + 256 + 2 * tn * 128 * 2
     head = [FAKE] * 4 + [None] + [FAKE] * 2 + [None] + [FAKE] * 3
     assert L.spa2_bwd(C.byref(d), *head, FAKE, n.value - 1, None) == _lib.E_WORKSPACE
     assert L.spa2_bwd(C.byref(d), *head, None, n.value, None) == _lib.E_WORKSPACE
+    # the staged dQ passes check the same size
+    st = [FAKE] * 5  # q k v lse dout
+    assert L.spa2_bwd_dq(C.byref(d), *st, FAKE, n.value - 1, None, FAKE, None) == _lib.E_WORKSPACE
+    rowterm = [FAKE] * 4 + [None] + [FAKE] * 2 + [None]
+    assert L.spa2_bwd_dq_rowterm(C.byref(d), *rowterm, FAKE, n.value - 1, FAKE,
+                                 None) == _lib.E_WORKSPACE
+    # fp32 keeps no mean keys; 128-key blocks run two 64-key tiles each
+    assert L.spa2_bwd_workspace_size(C.byref(good(dtype=_lib.F32)), C.byref(n)) == _lib.OK
+    assert n.value == 2 * 1000 * 4
+    assert L.spa2_bwd_workspace_size(C.byref(good(BKV=128, D=64)), C.byref(n)) == _lib.OK
+    assert n.value == 2 * 1000 * 4 + 256 + 2 * (2 * 8) * 64 * 2
 
 
 def test_bwd_noalloc_validation():
@@ -170,10 +184,20 @@ def test_bwd_noalloc_validation():
     a = list(args)
     a[0] = ODD
     assert L.spa2_bwd_noalloc(C.byref(good()), *a) == _lib.E_ALIGN
-    rows = _lib.NOALLOC_SCRATCH_BYTES // 4
-    big = good(B=1, H=rows // 65536 + 1, N=65536)
+    # the scratch holds the whole backward workspace: 40 heads of 75,600 tokens fit, at
+    # 64- and 32-key blocks; 80 heads do not, nor a workspace one step over the size
+    cap = _lib.NOALLOC_SCRATCH_BYTES
+    for kw in (dict(H=40, N=75600), dict(H=40, N=75600, BKV=128), dict(H=24, N=75600, BKV=32)):
+        assert L.spa2_bwd_workspace_bytes(C.byref(good(**kw))) <= cap, kw
+    big = good(B=1, H=80, N=75600)
+    assert L.spa2_bwd_workspace_bytes(C.byref(big)) > cap
     assert L.spa2_bwd_noalloc(C.byref(big), *args) == _lib.E_SCRATCH
-    assert L.spa2_bwd_noalloc(C.byref(good(B=2, H=rows // 65536, N=65536)), *args) == _lib.E_SCRATCH
+    assert L.spa2_bwd_noalloc(C.byref(good(B=2, H=40, N=75600)), *args) == _lib.E_SCRATCH
+    # fp32 (no mean keys): the largest head count whose row term fits, and one more
+    h = cap // (4 * 65536)
+    assert L.spa2_bwd_workspace_bytes(C.byref(good(H=h, N=65536, dtype=_lib.F32))) == cap
+    assert L.spa2_bwd_noalloc(C.byref(good(H=h + 1, N=65536, dtype=_lib.F32)),
+                              *args) == _lib.E_SCRATCH
 
 
 def test_bwd_workspace_bytes():
@@ -181,10 +205,13 @@ def test_bwd_workspace_bytes():
     descriptor, and is 0 for an invalid descriptor or NULL."""
     L = _lib.lib()
     n = C.c_size_t(0)
-    for kw in (dict(), dict(B=2, H=3, N=777, D=64, dtype=_lib.F32), dict(N=75600, H=40)):
+    for kw in (dict(), dict(B=2, H=3, N=777, D=64, dtype=_lib.F32), dict(N=75600, H=40),
+               dict(N=777, BKV=32, D=64)):
         d = good(**kw)
         assert L.spa2_bwd_workspace_size(C.byref(d), C.byref(n)) == _lib.OK
-        assert L.spa2_bwd_workspace_bytes(C.byref(d)) == n.value == d.B * d.H * d.N * 4
+        tiles = -(-d.N // d.BKV) * (2 if d.BKV == 128 else 1)
+        kmean = 256 + d.B * d.H * tiles * d.D * 2 if d.dtype == _lib.BF16 else 0
+        assert L.spa2_bwd_workspace_bytes(C.byref(d)) == n.value == d.B * d.H * d.N * 4 + kmean
     assert L.spa2_bwd_workspace_bytes(C.byref(good(D=96))) == 0
     assert L.spa2_bwd_workspace_bytes(C.byref(good(dtype=9))) == 0
     assert L.spa2_bwd_workspace_bytes(None) == 0

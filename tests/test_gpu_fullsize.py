@@ -96,20 +96,22 @@ def test_staged_backward_equals_bwd(wan13b):
     of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
     o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
     g1 = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
-    dvec = torch.empty_like(lse)
-    dq = spa2.bwd_dq_rowterm(d["q"], d["k"], d["v"], o, lse, d["do"], dvec, bm,
+    ws = spa2.bwd_workspace(d["q"], bm.bq, bm.bkv)
+    dvec = spa2.row_term(ws, d["q"])
+    dq = spa2.bwd_dq_rowterm(d["q"], d["k"], d["v"], o, lse, d["do"], ws, bm,
                              torch.empty_like(o), o_f32=of)
     dk, dv = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec, bm,
                            torch.empty_like(o), torch.empty_like(o))
     for a, b in zip(g1, (dq, dk, dv)):
         assert torch.equal(a, b)
-    dvec3 = torch.empty_like(lse)
+    ws3 = spa2.bwd_workspace(d["q"], bm.bq, bm.bkv)
+    dvec3 = spa2.row_term(ws3, d["q"])
     spa2.bwd_prep(o, d["do"], dvec3, o_f32=of)
     scale = dvec.abs().max().item()
     assert (dvec3 - dvec).abs().max().item() <= 1e-5 * scale
     dk3, dv3 = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm,
                              torch.empty_like(o), torch.empty_like(o))
-    dq3 = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm, torch.empty_like(o))
+    dq3 = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], ws3, bm, torch.empty_like(o))
     for nm, a, b in (("dQ", dq, dq3), ("dK", dk, dk3), ("dV", dv, dv3)):
         a, b = a.float(), b.float()
         rel = ((a - b).norm() / a.norm()).item()

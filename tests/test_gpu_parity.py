@@ -353,8 +353,9 @@ def test_staged_backward(name):
     of = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
     o, lse = spa2.fwd(d["q"], d["k"], d["v"], bm, o_f32=of)
     g1 = spa2.bwd(d["q"], d["k"], d["v"], o, lse, d["do"], bm, o_f32=of)
-    dvec = torch.empty_like(lse)
-    dq = spa2.bwd_dq_rowterm(d["q"], d["k"], d["v"], o, lse, d["do"], dvec, bm,
+    ws = spa2.bwd_workspace(d["q"], bm.bq, bm.bkv)
+    dvec = spa2.row_term(ws, d["q"])
+    dq = spa2.bwd_dq_rowterm(d["q"], d["k"], d["v"], o, lse, d["do"], ws, bm,
                              torch.empty_like(o), o_f32=of)
     dk, dv = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec, bm,
                            torch.empty_like(o), torch.empty_like(o))
@@ -363,11 +364,12 @@ def test_staged_backward(name):
     # row term against its definition, rowsum(dO * O) in float64
     want = (d["do"].double() * of.double()).sum(-1)
     assert torch.allclose(dvec.double(), want, rtol=1e-5, atol=1e-6 * want.abs().max().item())
-    dvec3 = torch.empty_like(lse)
+    ws3 = spa2.bwd_workspace(d["q"], bm.bq, bm.bkv)
+    dvec3 = spa2.row_term(ws3, d["q"])
     spa2.bwd_prep(o, d["do"], dvec3, o_f32=of)
     dk3, dv3 = spa2.bwd_dkdv(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm,
                              torch.empty_like(o), torch.empty_like(o))
-    dq3 = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], dvec3, bm, torch.empty_like(o))
+    dq3 = spa2.bwd_dq(d["q"], d["k"], d["v"], lse, d["do"], ws3, bm, torch.empty_like(o))
     for nm, got, want, blk in (("dQ", dq3, r["dq"], r["bq"]), ("dK", dk3, r["dk"], r["bkv"]),
                                ("dV", dv3, r["dv"], r["bkv"])):
         gu.check_close(nm, gu.to_f64(got), want, r["inp"].dtype, block=blk)
