@@ -559,8 +559,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
       const int e = w * 64 + l;
       const int r = min(i * BQ + (e % BQ), N - 1);
       const float* src = (e < BQ ? LSE : DV) + r;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (SPA2_LDS void*)(stage + 2 * QTile::kBytes + w * 256), 4, 0, 0);
+      lds_dma4(src, __builtin_amdgcn_readfirstlane(lds_address(stage + 2 * QTile::kBytes + w * 256)));
     }
   };
   if (cnt > 0) issue(stage0, block_at(0, 0));

@@ -36,6 +36,32 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(size_t)(const SPA2_LDS char*)p;
+}
+// Direct-to-LDS loads (global_load_lds): lane l's 16 (or 4) bytes from g land at
+// lds + 16 l (4 l); lds must be wave-uniform. They are written as inline asm on purpose:
+// the compiler's wait-count pass treats an outstanding builtin direct-to-LDS load as an
+// LDS access that completes out of order, and then waits for every LDS read with
+// lgkmcnt(0) until the load is done (which serialises the operand reads of the block
+// being computed with the matrix instructions). The asm writes no register (M0 aside), so
+// nothing the compiler allocates can be overwritten in flight; completion is waited for
+// explicitly with wait_vmem() (vmcnt(0)) before the barrier that publishes the tile, and
+// extra outstanding loads only make the compiler's own vmcnt waits stricter.
+__device__ __forceinline__ void lds_dma16(const void* g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
 // Cross-lane exchange without LDS: v_permlane16_swap / v_permlane32_swap applied to two
 // copies of x leave, in every lane l, the values of lanes {l, l^16} (resp. {l, l^32}).
 __device__ __forceinline__ float xchg16(float x, bool take_max) {
@@ -272,8 +298,7 @@ struct Tile {
       const int row = f / kChunks, pc = f % kChunks;
       const int grow = min(row0 + row, nrows - 1);
       const T* g = src + (size_t)grow * D + ((pc ^ swz(row)) * (16 / (int)sizeof(T)));
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                       (SPA2_LDS void*)(base + i * 1024), 16, 0, 0);
+      lds_dma16(g, __builtin_amdgcn_readfirstlane(lds_address(base + i * 1024)));
     }
   }
 
@@ -299,8 +324,8 @@ struct Tile {
       const T* tile = src + (size_t)row0 * D;
 #pragma unroll
       for (int n = 0; n < kLoads; ++n)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + off[n]),
-                                         (SPA2_LDS void*)(base + (n * NW + wave) * 1024), 16, 0, 0);
+        lds_dma16(tile + off[n],
+                  __builtin_amdgcn_readfirstlane(lds_address(base + (n * NW + wave) * 1024)));
     }
     // general case: rows past nrows - 1 clamped
     __device__ __forceinline__ void issue_any(char* base, const T* src, int row0, int nrows,
