@@ -507,7 +507,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
 // At the end the query groups' partial sums are added through LDS.
 // ------------------------------------------------------------------------------------
 template <typename T, int D, int BQ, int BKV, int QSUB, bool DENSE, int NW, int KT>
-__global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int KW = BKV / (16 * KT);    // key groups (KT 16-key tiles per wave)
@@ -807,10 +807,23 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
       a.rowterm = 0;                                                                 \
     }                                                                                \
     if (stages & kBwdDkdv) {                                                         \
-      constexpr int nw = dkdv_waves<T, BQ, BK>(), kt = dkdv_key_tiles<T, BQ>();      \
-      if (!m) bwd_dkdv_kernel<T, D, BQ, BK, 0, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
-      else if (s.qsub()) bwd_dkdv_kernel<T, D, BQ, BK, 1, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
-      else bwd_dkdv_kernel<T, D, BQ, BK, 0, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+      constexpr int kt = dkdv_key_tiles<T, BQ>();                                    \
+      if constexpr (sizeof(T) == 2) {                                                \
+        /* 64-row query tiles, 4 waves: two workgroups share a CU */                 \
+        constexpr int nw = 4;                                                        \
+        if (!m) bwd_dkdv_kernel<T, D, 64, BK, 0, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+        else if (a.bq_block == 128) bwd_dkdv_kernel<T, D, 64, BK, 1, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+        else if (a.bq_block == 64) bwd_dkdv_kernel<T, D, 64, BK, 0, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+        else { /* 256-row blocks: two 128-row tiles */                                \
+          constexpr int nw2 = dkdv_waves<T, BQ, BK>();                               \
+          bwd_dkdv_kernel<T, D, BQ, BK, 1, false, nw2, kt><<<gk, 64 * nw2, 0, st>>>(a); \
+        }                                                                            \
+      } else {                                                                       \
+        constexpr int nw = dkdv_waves<T, BQ, BK>();                                  \
+        if (!m) bwd_dkdv_kernel<T, D, BQ, BK, 0, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+        else if (s.qsub()) bwd_dkdv_kernel<T, D, BQ, BK, 1, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+        else bwd_dkdv_kernel<T, D, BQ, BK, 0, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
+      }                                                                              \
     }                                                                                \
     if (stages & kBwdDq) launch_dq(std::integral_constant<int, nq>{});               \
   } while (0)
