@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void kmean_kernel(const bf16* __restrict__ k, 
 // sum_k r_k costs one add per element.
 // ------------------------------------------------------------------------------------
 template <typename T, int D, int BQ, int BKV, int KSUB, bool DENSE, int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int KTN = BKV / 16;  // 16-key tiles per key step (BQ x BKV tiles)
@@ -790,20 +790,33 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
   const int tiles = bwd_key_tiles(s);
 #define SPA2_BWD(T, D, BQ, BK)                                                       \
   do {                                                                               \
-    constexpr int nq = dq_waves<T, D, BQ, BK>();                                     \
-    auto launch_dq = [&](auto nqt) {                                                 \
-      constexpr int NQ = decltype(nqt)::value;                                       \
+    auto launch_dq = [&](auto bqt, auto nqt, dim3 grid) {                            \
+      constexpr int BQT = decltype(bqt)::value, NQ = decltype(nqt)::value;           \
       if constexpr (sizeof(T) == 2)                                                  \
         kmean_kernel<D, BK><<<dim3((unsigned)(s.BH() * tiles)), 256, 0, st>>>(       \
             (const bf16*)k, (bf16*)kmean, s.N, tiles);                                \
-      if (!m) bwd_dq_kernel<T, D, BQ, BK, 0, true, NQ><<<gq, 64 * NQ, 0, st>>>(a);  \
-      else if (s.ksub()) bwd_dq_kernel<T, D, BQ, BK, 1, false, NQ><<<gq, 64 * NQ, 0, st>>>(a); \
-      else bwd_dq_kernel<T, D, BQ, BK, 0, false, NQ><<<gq, 64 * NQ, 0, st>>>(a);    \
+      if (!m) bwd_dq_kernel<T, D, BQT, BK, 0, true, NQ><<<grid, 64 * NQ, 0, st>>>(a); \
+      else if (s.ksub()) bwd_dq_kernel<T, D, BQT, BK, 1, false, NQ><<<grid, 64 * NQ, 0, st>>>(a); \
+      else bwd_dq_kernel<T, D, BQT, BK, 0, false, NQ><<<grid, 64 * NQ, 0, st>>>(a);  \
+    };                                                                               \
+    auto run_dq = [&]() {                                                            \
+      if constexpr (sizeof(T) == 2) {                                                \
+        if (a.bq_block <= 128) { /* 64-row tiles: two workgroups share a CU */       \
+          a.qsub = a.bq_block == 128 ? 1 : 0;                                        \
+          launch_dq(std::integral_constant<int, 64>{},                               \
+                    std::integral_constant<int, dq_waves<T, D, 64, BK>()>{},         \
+                    dim3((unsigned)((s.BH() * s.Tm) << a.qsub)));                    \
+          a.qsub = s.qsub();                                                         \
+          return;                                                                    \
+        }                                                                            \
+      }                                                                              \
+      launch_dq(std::integral_constant<int, BQ>{},                                   \
+                std::integral_constant<int, dq_waves<T, D, BQ, BK>()>{}, gq);        \
     };                                                                               \
     if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);            \
     if (stages & kBwdDqRow) { /* dQ and the row term first: dK/dV reads dvec */      \
       a.rowterm = 1;                                                                 \
-      launch_dq(std::integral_constant<int, nq>{});                                  \
+      run_dq();                                                                      \
       a.rowterm = 0;                                                                 \
     }                                                                                \
     if (stages & kBwdDkdv) {                                                         \
@@ -825,7 +838,7 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
         else bwd_dkdv_kernel<T, D, BQ, BK, 0, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
       }                                                                              \
     }                                                                                \
-    if (stages & kBwdDq) launch_dq(std::integral_constant<int, nq>{});               \
+    if (stages & kBwdDq) run_dq();                                                   \
   } while (0)
 #define SPA2_BWD_BK(T, D, BQ)                                                        \
   do {                                                                               \
