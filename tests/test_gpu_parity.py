@@ -117,6 +117,29 @@ def test_pbar_and_mask(name):
                 assert list(ci[b, h, j, :col_cnt[b, h, j]]) == list(np.flatnonzero(gmask[b, h, :, j]))
 
 
+@pytest.mark.parametrize("n,bkv,d,seed", [(40000, 64, 64, 30), (79872, 64, 64, 31),
+                                          (41600, 32, 64, 28), (79936, 64, 128, 29)])
+def test_mask_long_rows(n, bkv, d, seed):
+    """Long rows (T_n = 625, 1248, 1300 and 1249, with ragged T_m; the selection kernel holds
+    16 or 32 blocks per lane): P-bar and the mask against the oracle, lists against the
+    mask."""
+    inp = synth.sink_inputs(1, 1, n, d, 64, seed=seed, dtype="bf16")
+    print(f"[long rows] n={n} bkv={bkv} d={d} T_n={-(-n // bkv)}", flush=True)
+    k, p = 0.02, 0.3
+    mask, infos = gu.oracle_masks(inp, 128, bkv, k, p)
+    q, kk = gu.to_dev(inp.q), gu.to_dev(inp.k)
+    bm, pbar = spa2.mask(q, kk, k, p, 128, bkv, return_pbar=True)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(pbar.cpu().numpy()[0, 0], infos[0]["pbar"], rtol=1e-12, atol=1e-300)
+    gmask = bm.mask.cpu().numpy().astype(bool)
+    cls = gu.classify_mask(gmask, mask, infos)
+    print(f"[long rows] mask mismatches: {cls}")
+    assert cls["other"] == 0 and cls["k_band"] == 0, cls
+    row_cnt, col_cnt = gu.lists_from_mask(gmask)
+    assert np.array_equal(bm.row_cnt.cpu().numpy(), row_cnt)
+    assert np.array_equal(bm.col_cnt.cpu().numpy(), col_cnt)
+
+
 @pytest.mark.parametrize("name", CASES)
 def test_select_on_oracle_pbar(name):
     """The selection kernel alone, fed the oracle's own P-bar: the same values on both
