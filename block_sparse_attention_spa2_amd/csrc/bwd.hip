@@ -174,9 +174,8 @@ __global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel
 
   const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // paired XCDs, unless a block runs as two tiles (they stay on one XCD, sharing its L2)
-  const int pos = a.qsub ? xcd_item(blockIdx.x, (a.BH * a.Tm) << a.qsub)
-                         : xcd_item_paired(blockIdx.x, a.BH * a.Tm);
+  // paired XCDs; the tiles of one block stay on one XCD, sharing its L2
+  const int pos = xcd_item_paired_tiles(blockIdx.x, (a.BH * a.Tm) << a.qsub, a.qsub);
   const int ppos = pos >> a.qsub;  // this query tile's block, in scheduling order
   const int item = a.row_order ? __builtin_amdgcn_readfirstlane(a.row_order[ppos]) : ppos;
   const int bh = item / a.Tm, qb = item % a.Tm;
@@ -800,18 +799,16 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
       else bwd_dq_kernel<T, D, BQT, BK, 0, false, NQ><<<grid, 64 * NQ, 0, st>>>(a);  \
     };                                                                               \
     auto run_dq = [&]() {                                                            \
-      if constexpr (sizeof(T) == 2) {                                                \
-        if (a.bq_block <= 128) { /* 64-row tiles: two workgroups share a CU */       \
-          a.qsub = a.bq_block == 128 ? 1 : 0;                                        \
-          launch_dq(std::integral_constant<int, 64>{},                               \
-                    std::integral_constant<int, dq_waves<T, D, 64, BK>()>{},         \
-                    dim3((unsigned)((s.BH() * s.Tm) << a.qsub)));                    \
-          a.qsub = s.qsub();                                                         \
-          return;                                                                    \
-        }                                                                            \
+      if constexpr (sizeof(T) == 2) { /* 64-row tiles: two workgroups share a CU */  \
+        a.qsub = a.bq_block == 256 ? 2 : a.bq_block == 128 ? 1 : 0;                  \
+        launch_dq(std::integral_constant<int, 64>{},                                 \
+                  std::integral_constant<int, dq_waves<T, D, 64, BK>()>{},           \
+                  dim3((unsigned)((s.BH() * s.Tm) << a.qsub)));                      \
+        a.qsub = s.qsub();                                                           \
+      } else {                                                                       \
+        launch_dq(std::integral_constant<int, BQ>{},                                 \
+                  std::integral_constant<int, dq_waves<T, D, BQ, BK>()>{}, gq);      \
       }                                                                              \
-      launch_dq(std::integral_constant<int, BQ>{},                                   \
-                std::integral_constant<int, dq_waves<T, D, BQ, BK>()>{}, gq);        \
     };                                                                               \
     if (stages & kBwdPrep) bwd_pre_kernel<T, D><<<gpre, 256, 0, st>>>(a);            \
     if (stages & kBwdDqRow) { /* dQ and the row term first: dK/dV reads dvec */      \
@@ -827,10 +824,7 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
         if (!m) bwd_dkdv_kernel<T, D, 64, BK, 0, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
         else if (a.bq_block == 128) bwd_dkdv_kernel<T, D, 64, BK, 1, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
         else if (a.bq_block == 64) bwd_dkdv_kernel<T, D, 64, BK, 0, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
-        else { /* 256-row blocks: two 128-row tiles */                                \
-          constexpr int nw2 = dkdv_waves<T, BQ, BK>();                               \
-          bwd_dkdv_kernel<T, D, BQ, BK, 1, false, nw2, kt><<<gk, 64 * nw2, 0, st>>>(a); \
-        }                                                                            \
+        else bwd_dkdv_kernel<T, D, 64, BK, 2, false, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \
       } else {                                                                       \
         constexpr int nw = dkdv_waves<T, BQ, BK>();                                  \
         if (!m) bwd_dkdv_kernel<T, D, BQ, BK, 0, true, nw, kt><<<gk, 64 * nw, 0, st>>>(a); \

@@ -103,6 +103,18 @@ __device__ __forceinline__ int xcd_item_paired(int bid, int items) {
   return x0 * q + min(x0, r) + 2 * slot + (x & 1);
 }
 
+// The paired walk for work items that are 2^sub consecutive tiles of one block (items =
+// blocks << sub): the two XCDs of a pair alternate whole blocks, so a block's tiles run on
+// one XCD and share its L2. A bijection when items is a multiple of 8 << sub (each XCD's
+// range is then whole blocks); otherwise the plain contiguous ranges of xcd_item.
+__device__ __forceinline__ int xcd_item_paired_tiles(int bid, int items, int sub) {
+  if (sub == 0) return xcd_item_paired(bid, items);
+  if (items & ((8 << sub) - 1)) return xcd_item(bid, items);
+  const int q = items >> 3, x = bid & 7, slot = bid >> 3;
+  const int x0 = x & ~1;
+  return x0 * q + ((2 * (slot >> sub) + (x & 1)) << sub) + (slot & ((1 << sub) - 1));
+}
+
 // The kept-block list of one work item, read ahead with scalar loads. The lists are not
 // written while a kernel runs, so they are read through the constant address space: the
 // wait for an entry is an lgkmcnt wait, never a wait for the direct-to-LDS tile loads in
@@ -130,26 +142,28 @@ struct BlockQueue {
 };
 
 // Tiles of a kept-block list when every kept block covers 2^S consecutive tiles of the
-// kernel (S = 0 or 1; S = 1 for 128-key blocks run as two 64-key tiles, or 256-row blocks
-// as two 128-row tiles): tile t is sub-tile (t mod 2^S) of list entry t >> S. tile(t, i)
-// is the tile at position t + i (i <= 2; entries past the list read as block 0);
-// advance(t) moves from t to t + 1. t must be wave-uniform. S is a template parameter so
-// that the plain case (S = 0) is exactly BlockQueue, with no branch in the loop.
+// kernel (S = 0, 1 or 2; e.g. S = 1 for 128-key blocks run as two 64-key tiles, S = 2 for
+// 256-row blocks run as four 64-row tiles): tile t is sub-tile (t mod 2^S) of list entry
+// t >> S. tile(t, i) is the tile at position t + i (i <= 2; entries past the list read as
+// block 0); advance(t) moves from t to t + 1. t must be wave-uniform. S is a template
+// parameter so that the plain case (S = 0) is exactly BlockQueue, with no branch in the
+// loop.
 template <int S>
 struct TileQueue {
+  static_assert(S >= 0 && S <= 2, "up to four tiles per block");
   BlockQueue<2> bq;
   __device__ __forceinline__ void init(const int32_t* l, int blocks) { bq.init(l, blocks); }
   __device__ __forceinline__ int tile(int t, int i) const {
     if constexpr (S == 0) {
       return bq.q[i];
     } else {
-      const int u = (t & 1) + i;
-      return (bq.q[u >> 1] << 1) + (u & 1);
+      const int u = (t & ((1 << S) - 1)) + i;  // at most 2^S + 1: entry index u >> S <= 1
+      return (bq.q[u >> S] << S) + (u & ((1 << S) - 1));
     }
   }
   __device__ __forceinline__ void advance(int t) {
     if constexpr (S == 0) bq.advance(t);
-    else if (t & 1) bq.advance(t >> 1);
+    else if ((t & ((1 << S) - 1)) == (1 << S) - 1) bq.advance(t >> S);
   }
 };
 
