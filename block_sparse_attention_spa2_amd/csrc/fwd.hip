@@ -44,6 +44,29 @@ struct FwdArgs {
 // Rescale threshold in log2 units: probabilities stay below 2^8 between rescales.
 constexpr float kRescaleSlack = 8.0f;
 
+// Maxima of scores (finite, or -inf for keys past N) as plain v_max3_f32 / v_max_f32:
+// fmaxf would first canonicalise every operand that the compiler cannot prove canonical
+// (all matrix-unit results), doubling the instruction count of the block maximum.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// max over the four lanes that share a query column (l, l^16, l^32, l^48)
+__device__ __forceinline__ float max4_raw(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = max_raw(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  u = __builtin_bit_cast(unsigned, x);
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return max_raw(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 // Tiles: BQ query rows per workgroup, BKV keys per step (32 or 64). A mask block of 256
 // rows runs as two workgroups (query tiles), a 128-key block as two key steps.
 template <typename T, int D, int BQ, int BKV, int KSUB, bool DENSE, int NW>
@@ -155,11 +178,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     bool raise = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float m = -INFINITY;
+      // this lane's KTN x 4 scores of the column, two new ones per v_max3
+      float m = max3_raw(s[0][qt][0], s[0][qt][1], s[0][qt][2]);
 #pragma unroll
-      for (int kt = 0; kt < KTN; ++kt)
-        m = fmaxf(m, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
-      mx[qt] = max4(m) * a.scale_log2;
+      for (int e = 3; e < 4 * KTN; e += 2) {
+        const float x0 = s[e / 4][qt][e % 4];
+        m = e + 1 < 4 * KTN ? max3_raw(m, x0, s[(e + 1) / 4][qt][(e + 1) % 4]) : max_raw(m, x0);
+      }
+      mx[qt] = max4_raw(m) * a.scale_log2;
       raise |= mx[qt] > mrow[qt] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: some row needs a new max
