@@ -13,11 +13,13 @@
 //             like the forward; K_j and V_j are staged in LDS; optionally computes Dv of
 //             its rows first (the row term) and writes it for the dK/dV pass;
 //   bwd_dkdv  one workgroup per key tile, looping over the query tiles that keep it
-//             (column lists); the waves split the pair into key groups x query groups,
-//             Q_i and dO_i are staged in LDS, and the query groups' partial dK/dV are
-//             summed through LDS at the end.
-// Tiles are at most 128 query rows and 64 keys; a 256-row or 128-key mask block is two
-// consecutive tiles over the same list entry (TileQueue).
+//             (column lists); the waves split the pair into key groups (x query groups
+//             for fp32, whose partial dK/dV are summed through LDS at the end); Q_i and
+//             dO_i are staged in LDS.
+// bf16 runs both passes on 64-row query tiles with four waves, small enough in LDS for two
+// workgroups to share a CU, so that one hides the other's fixed cost (list lookups, first
+// tile, fragment loads, epilogue). Tiles are at most 128 query rows and 64 keys; a larger
+// mask block is two or four consecutive tiles over the same list entry (TileQueue).
 #include <math.h>
 
 #include <type_traits>
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel
   using CM = Tile<T, 32, D>;  // c_j of one batch of eight blocks, four copies (bf16 only)
   // K/V stages in separate LDS variables, named statically (see the forward kernel). The
   // code also runs three stages (loads issued two blocks ahead, partial vmcnt waits), which
-  // measured slower than two with eight waves per workgroup.
+  // measured slower than two (with eight-wave workgroups, one per CU).
   constexpr int kStageBytes = 2 * KV::kBytes;
   constexpr int NS = 2;
   __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
@@ -495,15 +497,16 @@ __global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel
 
 // ------------------------------------------------------------------------------------
 // dK, dV: per key block, over the query blocks that keep it (column lists).
-// NW waves split each (key block, query block) pair into KW key groups of 16 KT keys
+// NW waves split each (key block, query tile) pair into KW key groups of 16 KT keys
 // times QW = NW / KW query groups, so each wave reads only its rows of Q_i and dO_i from
-// LDS (in both layouts). Eight waves (16 keys each, two waves per SIMD) keep the register
-// footprint of a wave small enough for two of them to share a SIMD; four waves (32 keys
-// each) halve the LDS traffic per matrix instruction instead. Q_i, dO_i and the row
-// statistics stream into LDS with global_load_lds, one block ahead.
+// LDS (in both layouts). bf16: four waves of 16 keys over 64-row query tiles (QW = 1),
+// 246 registers and 65.5 KB of LDS, two workgroups per CU (two waves per SIMD); 32 keys
+// per wave would halve the LDS traffic per matrix instruction but needs more registers
+// than two waves per SIMD allow. Q_i, dO_i and the row statistics stream into LDS with
+// direct-to-LDS loads, one tile ahead.
 //   S = Q K^T, dP = dO V^T (A = Q, dO rows from LDS; B = K, V in registers),
 //   dS = P * (dP - Dv), dV^T += dO^T P, dK^T += Q^T dS (A via transpose reads).
-// At the end the query groups' partial sums are added through LDS.
+// With QW > 1 (fp32) the query groups' partial sums are added through LDS at the end.
 // ------------------------------------------------------------------------------------
 template <typename T, int D, int BQ, int BKV, int QSUB, bool DENSE, int NW, int KT>
 __global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
@@ -755,12 +758,12 @@ __global__ __launch_bounds__(64 * NW, sizeof(T) == 2 ? 2 : 1) void bwd_dkdv_kern
   }
 }
 
-// dK/dV work split: bf16 runs eight waves per workgroup (two per SIMD) of one 16-key tile
-// each (32 keys per wave would need more than the 256 registers of two waves per SIMD);
-// fp32 runs four waves of two tiles.
+// dK/dV work split: bf16 runs four waves of one 16-key tile each over 64-row query tiles
+// (launch_bwd); fp32 runs waves of two 16-key tiles.
 template <typename T, int BQ>
 constexpr int dkdv_key_tiles() { return sizeof(T) == 2 ? 1 : 2; }
-// dK/dV waves: 2 x 16-row query tiles per wave at least (the products reduce over 32 rows)
+// dK/dV waves of the 128-row-tile form (fp32): 2 x 16-row query tiles per wave at least
+// (the products reduce over 32 rows)
 template <typename T, int BQ, int BKV>
 constexpr int dkdv_waves() {
   return (sizeof(T) == 2 ? 8 : 4) / (BKV == 32 && BQ == 64 ? 2 : 1);
