@@ -14,8 +14,9 @@
 // with one barrier per tile. Scores are computed transposed, S^T = K Q^T (operand A = K rows from LDS,
 // operand B = Q held in registers), so each lane owns one query column and the
 // online-softmax state is lane local (the row max needs the 4 lanes that share the
-// column, combined with VALU lane swaps). P^T leaves the accumulators directly as the
-// B operand of O^T = V^T P^T; V^T comes from row-major LDS through transpose reads.
+// column, combined with VALU lane swaps, but only when it is raised). P^T leaves the
+// accumulators directly as the B operand of O^T = V^T P^T; V^T comes from row-major LDS
+// through transpose reads.
 // The running max is only raised (and O rescaled) when a row's block max exceeds it by
 // more than 2^8, so most blocks skip the rescale; the final normalisation is exact.
 #include <math.h>
@@ -44,17 +45,40 @@ struct FwdArgs {
 // Rescale threshold in log2 units: probabilities stay below 2^8 between rescales.
 constexpr float kRescaleSlack = 8.0f;
 
-// Maxima of scores (finite, or -inf for keys past N) as plain v_max3_f32 / v_max_f32:
-// fmaxf would first canonicalise every operand that the compiler cannot prove canonical
-// (all matrix-unit results), doubling the instruction count of the block maximum.
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// Maxima of scores (finite, or -inf for keys past N) as plain v_max3_f32 / v_max_f32 in
+// inline asm: fmaxf would first canonicalise every operand that the compiler cannot prove
+// canonical (all matrix-unit results), doubling the instruction count of the block maximum.
 __device__ __forceinline__ float max_raw(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// Maximum of a lane's 16 (or 8) scores of one column as two interleaved v_max3 chains in
+// one asm block (separate asm statements get a wait state between each pair).
+__device__ __forceinline__ float lane_max16(const f32x4& a, const f32x4& b, const f32x4& c,
+                                            const f32x4& d) {
+  float r, t;
+  asm("v_max3_f32 %0, %2, %3, %4\n\t"
+      "v_max3_f32 %1, %5, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max3_f32 %1, %1, %10, %11\n\t"
+      "v_max3_f32 %0, %0, %12, %13\n\t"
+      "v_max3_f32 %1, %1, %14, %15\n\t"
+      "v_max3_f32 %0, %0, %16, %17\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "=&v"(r), "=&v"(t)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]),
+        "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]));
+  return r;
+}
+__device__ __forceinline__ float lane_max8(const f32x4& a, const f32x4& b) {
+  float r, t;
+  asm("v_max3_f32 %0, %2, %3, %4\n\t"
+      "v_max3_f32 %1, %5, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "=&v"(r), "=&v"(t)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
   return r;
 }
 // max over the four lanes that share a query column (l, l^16, l^32, l^48)
@@ -130,10 +154,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[QT], lrow[QT];
+  // running max (log2 units) and its finite stand-in for the exponent (0 while no key of
+  // the column has been seen), both changed only when the max is raised
+  float mrow[QT], mref[QT], lrow[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     mrow[qt] = -INFINITY;
+    mref[qt] = 0.f;
     lrow[qt] = 0.f;
   }
 
@@ -173,27 +200,28 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
             for (int qt = 0; qt < QT; ++qt) s[kt][qt][e] = -INFINITY;
     }
 
-    // online softmax, per query column (base-2 exponent with the scale folded in)
+    // online softmax, per query column (base-2 exponent with the scale folded in). Whether
+    // some column's block max exceeds its running max by the slack is decided from each
+    // lane's own maximum (a column exceeds it iff one of its four lanes does); the column
+    // max over the four lanes is formed only when the running max is raised.
     float mx[QT];
     bool raise = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      // this lane's KTN x 4 scores of the column, two new ones per v_max3
-      float m = max3_raw(s[0][qt][0], s[0][qt][1], s[0][qt][2]);
-#pragma unroll
-      for (int e = 3; e < 4 * KTN; e += 2) {
-        const float x0 = s[e / 4][qt][e % 4];
-        m = e + 1 < 4 * KTN ? max3_raw(m, x0, s[(e + 1) / 4][qt][(e + 1) % 4]) : max_raw(m, x0);
-      }
-      mx[qt] = max4_raw(m) * a.scale_log2;
-      raise |= mx[qt] > mrow[qt] + kRescaleSlack;
+      // this lane's KTN x 4 scores of the column
+      float m;
+      if constexpr (KTN == 4) m = lane_max16(s[0][qt], s[1][qt], s[2][qt], s[3][qt]);
+      else m = lane_max8(s[0][qt], s[1][qt]);
+      mx[qt] = m;
+      raise |= m * a.scale_log2 > mrow[qt] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: some row needs a new max
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const float mnew = fmaxf(mrow[qt], mx[qt]);
+        const float mnew = fmaxf(mrow[qt], max4_raw(mx[qt]) * a.scale_log2);
         const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mnew);  // 0 on the first block
         mrow[qt] = mnew;
+        mref[qt] = mnew == -INFINITY ? 0.f : mnew;
         lrow[qt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
@@ -201,13 +229,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const float mref = mrow[qt] == -INFINITY ? 0.f : mrow[qt];
       float ls = 0.f;
 #pragma unroll
       for (int kt = 0; kt < KTN; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][e], a.scale_log2, -mref));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][e], a.scale_log2, -mref[qt]));
           s[kt][qt][e] = p;
           ls += p;
         }
