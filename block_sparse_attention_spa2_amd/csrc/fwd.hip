@@ -7,12 +7,12 @@
 // fetched.
 //
 // One workgroup (4 waves) per query tile of 64 or 128 rows (a 256-row block is two
-// tiles); two workgroups share a CU (2 waves per SIMD, so one wave's softmax overlaps
-// the other's matrix work). Wave w owns a quarter of the tile's rows. Key tiles of 32 or
-// 64 rows (a 128-key block is two tiles) of K and V stream from global memory straight
+// tiles); two or three workgroups share a CU (one wave's softmax overlaps the others'
+// matrix work). Wave w owns a quarter of the tile's rows. Key tiles of 32 or 64 rows (a
+// larger key block is two or four tiles) of K and V stream from global memory straight
 // into a double-buffered, swizzled LDS tile (global_load_lds), issued one tile ahead,
-// with one barrier per tile. Scores are computed transposed, S^T = K Q^T (operand A = K rows from LDS,
-// operand B = Q held in registers), so each lane owns one query column and the
+// with one barrier per tile. Scores are computed transposed, S^T = K Q^T (operand A = K
+// rows from LDS, operand B = Q held in registers), so each lane owns one query column and the
 // online-softmax state is lane local (the row max needs the 4 lanes that share the
 // column, combined with VALU lane swaps, but only when it is raised). P^T leaves the
 // accumulators directly as the B operand of O^T = V^T P^T; V^T comes from row-major LDS
@@ -91,10 +91,19 @@ __device__ __forceinline__ float max4_raw(float x) {
   return max_raw(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
+// Workgroups per CU that the launch bounds ask for. bf16 at D = 128 with 128-row query
+// tiles steps through 32-key tiles: 32 KB of LDS and at most 168 registers per 4-wave
+// workgroup let three workgroups share a CU (three waves per SIMD), which hides more of
+// each wave's dependent S -> softmax -> P.V chain than two workgroups with 64-key tiles
+// (64 KB of LDS each).
+template <typename T, int D, int BQ, int BKV>
+constexpr int fwd_wgs_per_cu() { return sizeof(T) == 2 && D == 128 && BQ == 128 && BKV == 32 ? 3 : 2; }
+
 // Tiles: BQ query rows per workgroup, BKV keys per step (32 or 64). A mask block of 256
-// rows runs as two workgroups (query tiles), a 128-key block as two key steps.
+// rows runs as two workgroups (query tiles), a mask block of more keys than BKV as 2^KSUB
+// key steps.
 template <typename T, int D, int BQ, int BKV, int KSUB, bool DENSE, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * NW, (fwd_wgs_per_cu<T, D, BQ, BKV>())) void fwd_kernel(FwdArgs a) {
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int QT = BQ / (16 * NW);  // 16-row query tiles per wave
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
   // (the loop below is unrolled by two), so the compiler can tell that the loads into one
   // stage do not alias the reads of the other and does not wait for them early.
   // the epilogue stages half the fp32 O tile in each stage
-  constexpr int kStageBytes = 2 * KV::kBytes > BQ / 2 * D * 4 ? 2 * KV::kBytes : BQ / 2 * D * 4;
+  constexpr int kStageBytes = 2 * KV::kBytes;
   __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char stage1[kStageBytes];
 
@@ -264,98 +273,120 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_kernel(FwdArgs a) {
 
   // epilogue: normalise, then store O (and the unrounded copy) through LDS, so that every
   // global store writes whole 16-byte chunks of consecutive columns of a row (full cache
-  // lines) instead of 4 columns of 16 rows. The fp32 tile (BQ x D) goes into the two
-  // stages, rows [0, BQ/2) into stage0 and the rest into stage1, with the 16-byte chunks
-  // of row r XOR-swizzled by r mod 32 (conflict-free writes of 16 rows at a time).
+  // lines) instead of 4 columns of 16 rows. The fp32 tile (BQ x D) passes through the two
+  // stages in as many passes of kPassRows rows as they need (one for 64-key tiles, two
+  // for 32-key tiles): the first half of a pass's rows into stage0, the rest into
+  // stage1, with the 16-byte chunks of row r XOR-swizzled by r mod 32 (conflict-free
+  // writes of 16 rows at a time).
   float* lse = a.lse + (size_t)bh * N;
   constexpr int kRowChunks = D / 4;               // 16-byte fp32 chunks per row
-  constexpr int kHalfRows = BQ / 2;
-  static_assert(kHalfRows * D * 4 <= kStageBytes, "a stage holds half of the O tile");
-  auto chunk_at = [&](int r, int c) -> f32x4* {  // row r of the block, chunk c
+  constexpr int kFit = 2 * (kStageBytes / (D * 4));  // rows that the two stages hold
+  constexpr int kPassRows = kFit < BQ ? kFit : BQ;
+  constexpr int kHalfRows = kPassRows / 2;
+  static_assert(BQ % kPassRows == 0 && kPassRows % (16 * QT) == 0, "whole waves per pass");
+  auto chunk_at = [&](int r, int c) -> f32x4* {  // row r of the pass, chunk c
     char* base = r < kHalfRows ? stage0 : stage1;
     const int rr = r % kHalfRows;
     return reinterpret_cast<f32x4*>(base + rr * D * 4 + ((c ^ (rr & (kRowChunks - 1) & 31)) << 4));
   };
-  lds_barrier();  // every wave is done with the K/V stages
+  float inv[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int rl = w * 16 * QT + qt * 16 + c16;  // row within the block
-    const int row = r0 + rl;
+    const int row = r0 + w * 16 * QT + qt * 16 + c16;
     const float lt = sum4(lrow[qt]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *chunk_at(rl, dt * 4 + g) = oacc[dt][qt] * inv;
+    inv[qt] = lt > 0.f ? 1.f / lt : 0.f;
     if (g == 0 && row < N) lse[row] = lt > 0.f ? (mrow[qt] + __log2f(lt)) * kLn2 : -INFINITY;
   }
-  lds_barrier();
-  const int rows_here = min(BQ, N - r0);
-  T* O = (T*)a.o + head + (size_t)r0 * D;
   constexpr int kEpc = 16 / (int)sizeof(T);        // elements per 16-byte output chunk
-  constexpr int kOutChunks = BQ * D / kEpc;
-  for (int f = tid; f < kOutChunks; f += 64 * NW) {
-    const int r = f / (D / kEpc), c = f % (D / kEpc);
-    if (r >= rows_here) break;  // chunks are in row order
-    if constexpr (sizeof(T) == 2) {
-      const f32x4 lo = *chunk_at(r, 2 * c), hi = *chunk_at(r, 2 * c + 1);
-      bf16x8 ob;
+  for (int pr0 = 0; pr0 < BQ; pr0 += kPassRows) {
+    lds_barrier();  // the K/V stages, or the previous pass, are no longer read
+    if (w * 16 * QT >= pr0 && w * 16 * QT < pr0 + kPassRows) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ob[e] = (bf16)lo[e];
-        ob[4 + e] = (bf16)hi[e];
+      for (int qt = 0; qt < QT; ++qt) {
+        const int rl = w * 16 * QT + qt * 16 + c16 - pr0;  // row within the pass
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *chunk_at(rl, dt * 4 + g) = oacc[dt][qt] * inv[qt];
       }
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ob),
-                                  reinterpret_cast<u32x4*>(O + (size_t)r * D + c * kEpc));
-    } else {
-      __builtin_nontemporal_store(*chunk_at(r, c), reinterpret_cast<f32x4*>(O + (size_t)r * D + c * kEpc));
     }
-  }
-  if (a.o_f32) {
-    float* Of = a.o_f32 + head + (size_t)r0 * D;
-    for (int f = tid; f < BQ * kRowChunks; f += 64 * NW) {
-      const int r = f / kRowChunks, c = f % kRowChunks;
-      if (r >= rows_here) break;
-      __builtin_nontemporal_store(*chunk_at(r, c), reinterpret_cast<f32x4*>(Of + (size_t)r * D + c * 4));
+    lds_barrier();
+    const int rows_here = min(kPassRows, N - r0 - pr0);
+    T* O = (T*)a.o + head + (size_t)(r0 + pr0) * D;
+    for (int f = tid; f < kPassRows * D / kEpc; f += 64 * NW) {
+      const int r = f / (D / kEpc), c = f % (D / kEpc);
+      if (r >= rows_here) break;  // chunks are in row order
+      if constexpr (sizeof(T) == 2) {
+        const f32x4 lo = *chunk_at(r, 2 * c), hi = *chunk_at(r, 2 * c + 1);
+        bf16x8 ob;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ob[e] = (bf16)lo[e];
+          ob[4 + e] = (bf16)hi[e];
+        }
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, ob),
+                                    reinterpret_cast<u32x4*>(O + (size_t)r * D + c * kEpc));
+      } else {
+        __builtin_nontemporal_store(*chunk_at(r, c), reinterpret_cast<f32x4*>(O + (size_t)r * D + c * kEpc));
+      }
+    }
+    if (a.o_f32) {
+      float* Of = a.o_f32 + head + (size_t)(r0 + pr0) * D;
+      for (int f = tid; f < kPassRows * kRowChunks; f += 64 * NW) {
+        const int r = f / kRowChunks, c = f % kRowChunks;
+        if (r >= rows_here) break;
+        __builtin_nontemporal_store(*chunk_at(r, c), reinterpret_cast<f32x4*>(Of + (size_t)r * D + c * 4));
+      }
     }
   }
 }
 
-// Waves per workgroup. Four (32 query rows each for 128-row blocks, two workgroups and so
-// two waves per SIMD) measured faster than eight waves of 16 rows (four per SIMD), which
-// read every K/V tile from LDS twice as often per matrix instruction.
+// Waves per workgroup. Four (32 query rows each for 128-row blocks) measured faster than
+// eight waves of 16 rows, which read every K/V tile from LDS twice as often per matrix
+// instruction.
 template <typename T, int BQ>
 constexpr int fwd_waves() { return 4; }
+
+template <typename T, int D, int BQ, int BK>
+void launch_fwd_tile(const Shape& s, const FwdArgs& a, hipStream_t st) {
+  constexpr int nw = fwd_waves<T, BQ>();
+  const dim3 grid(a.items), block(64 * nw);
+  const int steps = s.BKV / BK;  // key steps per mask block: 1, 2 or 4
+  if (!a.row_cnt) {
+    fwd_kernel<T, D, BQ, BK, 0, true, nw><<<grid, block, 0, st>>>(a);
+  } else if constexpr (BK == 32) {
+    if (steps == 4) fwd_kernel<T, D, BQ, BK, 2, false, nw><<<grid, block, 0, st>>>(a);
+    else if (steps == 2) fwd_kernel<T, D, BQ, BK, 1, false, nw><<<grid, block, 0, st>>>(a);
+    else fwd_kernel<T, D, BQ, BK, 0, false, nw><<<grid, block, 0, st>>>(a);
+  } else {
+    if (steps == 2) fwd_kernel<T, D, BQ, BK, 1, false, nw><<<grid, block, 0, st>>>(a);
+    else fwd_kernel<T, D, BQ, BK, 0, false, nw><<<grid, block, 0, st>>>(a);
+  }
+}
+
+template <typename T, int D, int BQ>
+void launch_fwd_bq(const Shape& s, const FwdArgs& a, hipStream_t st) {
+  if constexpr (fwd_wgs_per_cu<T, D, BQ, 32>() == 3) launch_fwd_tile<T, D, BQ, 32>(s, a, st);
+  else if (s.bkv_tile() == 32) launch_fwd_tile<T, D, BQ, 32>(s, a, st);
+  else launch_fwd_tile<T, D, BQ, 64>(s, a, st);
+}
+
+template <typename T, int D>
+void launch_fwd_d(const Shape& s, const FwdArgs& a, hipStream_t st) {
+  if (s.bq_tile() == 64) launch_fwd_bq<T, D, 64>(s, a, st);
+  else launch_fwd_bq<T, D, 128>(s, a, st);
+}
 
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const int32_t* row_cnt, const int32_t* row_idx, const int32_t* row_order,
                       void* o, float* lse, float* o_f32, hipStream_t st) {
   const int items = (s.BH() * s.Tm) << s.qsub();
-  FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, row_cnt ? row_order : nullptr, s.N, s.Tm,
-            s.Tn, items, s.BQ, s.qsub(),
-            (float)(1.4426950408889634 / sqrt((double)s.D))};
-  const dim3 grid(items);
-#define SPA2_FWD(T, D, BQ, BK)                                                   \
-  do {                                                                           \
-    constexpr int nw = fwd_waves<T, BQ>();                                       \
-    if (!row_cnt) fwd_kernel<T, D, BQ, BK, 0, true, nw><<<grid, 64 * nw, 0, st>>>(a); \
-    else if (s.ksub()) fwd_kernel<T, D, BQ, BK, 1, false, nw><<<grid, 64 * nw, 0, st>>>(a); \
-    else fwd_kernel<T, D, BQ, BK, 0, false, nw><<<grid, 64 * nw, 0, st>>>(a);   \
-  } while (0)
-#define SPA2_FWD_BK(T, D, BQ)                                                    \
-  do {                                                                           \
-    if (s.bkv_tile() == 32) SPA2_FWD(T, D, BQ, 32); else SPA2_FWD(T, D, BQ, 64); \
-  } while (0)
-#define SPA2_FWD_BQ(T, D)                                                        \
-  do {                                                                           \
-    if (s.bq_tile() == 64) SPA2_FWD_BK(T, D, 64); else SPA2_FWD_BK(T, D, 128);   \
-  } while (0)
+  const FwdArgs a{q, k, v, o, lse, o_f32, row_cnt, row_idx, row_cnt ? row_order : nullptr, s.N,
+                  s.Tm, s.Tn, items, s.BQ, s.qsub(),
+                  (float)(1.4426950408889634 / sqrt((double)s.D))};
   if (s.dtype == SPA2_BF16) {
-    if (s.D == 64) SPA2_FWD_BQ(bf16, 64); else SPA2_FWD_BQ(bf16, 128);
+    if (s.D == 64) launch_fwd_d<bf16, 64>(s, a, st); else launch_fwd_d<bf16, 128>(s, a, st);
   } else {
-    if (s.D == 64) SPA2_FWD_BQ(float, 64); else SPA2_FWD_BQ(float, 128);
+    if (s.D == 64) launch_fwd_d<float, 64>(s, a, st); else launch_fwd_d<float, 128>(s, a, st);
   }
-#undef SPA2_FWD_BQ
-#undef SPA2_FWD_BK
-#undef SPA2_FWD
   return hipGetLastError();
 }
 
