@@ -7,7 +7,7 @@
 // fetched.
 //
 // One workgroup (4 waves) per query tile of 64 or 128 rows (a 256-row block is two
-// tiles); two or three workgroups share a CU (one wave's softmax overlaps the others'
+// tiles); two to four workgroups share a CU (one wave's softmax overlaps the others'
 // matrix work). Wave w owns a quarter of the tile's rows. Key tiles of 32 or 64 rows (a
 // larger key block is two or four tiles) of K and V stream from global memory straight
 // into a double-buffered, swizzled LDS tile (global_load_lds), issued one tile ahead,
@@ -91,13 +91,15 @@ __device__ __forceinline__ float max4_raw(float x) {
   return max_raw(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
-// Workgroups per CU that the launch bounds ask for. bf16 at D = 128 with 128-row query
-// tiles steps through 32-key tiles: 32 KB of LDS and at most 168 registers per 4-wave
-// workgroup let three workgroups share a CU (three waves per SIMD), which hides more of
-// each wave's dependent S -> softmax -> P.V chain than two workgroups with 64-key tiles
-// (64 KB of LDS each).
+// Workgroups per CU that the launch bounds ask for. bf16 at D = 128 steps through 32-key
+// tiles: 32 KB of LDS and at most 168 registers per 4-wave workgroup of 128 query rows
+// (128 for 64 rows) let three (four) workgroups share a CU, which hides more of each
+// wave's dependent S -> softmax -> P.V chain than two workgroups with 64-key tiles (64 KB
+// of LDS each).
 template <typename T, int D, int BQ, int BKV>
-constexpr int fwd_wgs_per_cu() { return sizeof(T) == 2 && D == 128 && BQ == 128 && BKV == 32 ? 3 : 2; }
+constexpr int fwd_wgs_per_cu() {
+  return sizeof(T) == 2 && D == 128 && BKV == 32 ? (BQ == 128 ? 3 : 4) : 2;
+}
 
 // Tiles: BQ query rows per workgroup, BKV keys per step (32 or 64). A mask block of 256
 // rows runs as two workgroups (query tiles), a mask block of more keys than BKV as 2^KSUB
@@ -364,7 +366,7 @@ void launch_fwd_tile(const Shape& s, const FwdArgs& a, hipStream_t st) {
 
 template <typename T, int D, int BQ>
 void launch_fwd_bq(const Shape& s, const FwdArgs& a, hipStream_t st) {
-  if constexpr (fwd_wgs_per_cu<T, D, BQ, 32>() == 3) launch_fwd_tile<T, D, BQ, 32>(s, a, st);
+  if constexpr (fwd_wgs_per_cu<T, D, BQ, 32>() > 2) launch_fwd_tile<T, D, BQ, 32>(s, a, st);
   else if (s.bkv_tile() == 32) launch_fwd_tile<T, D, BQ, 32>(s, a, st);
   else launch_fwd_tile<T, D, BQ, 64>(s, a, st);
 }
