@@ -54,11 +54,16 @@ __device__ __forceinline__ float max_raw(float a, float b) {
   return r;
 }
 // Maximum of a lane's 16 (or 8) scores of one column as two interleaved v_max3 chains in
-// one asm block (separate asm statements get a wait state between each pair).
+// one asm block (separate asm statements get a wait state between each pair). The scores
+// come straight from matrix instructions: a vector instruction may read an MFMA result
+// only 8 wait states after the MFMA issues (16x16x32 bf16 on gfx950), and the compiler
+// inserts those wait states for its own instructions but not for inline asm, so each
+// block starts with s_nop 7.
 __device__ __forceinline__ float lane_max16(const f32x4& a, const f32x4& b, const f32x4& c,
                                             const f32x4& d) {
   float r, t;
-  asm("v_max3_f32 %0, %2, %3, %4\n\t"
+  asm("s_nop 7\n\t"
+      "v_max3_f32 %0, %2, %3, %4\n\t"
       "v_max3_f32 %1, %5, %6, %7\n\t"
       "v_max3_f32 %0, %0, %8, %9\n\t"
       "v_max3_f32 %1, %1, %10, %11\n\t"
@@ -73,7 +78,8 @@ __device__ __forceinline__ float lane_max16(const f32x4& a, const f32x4& b, cons
 }
 __device__ __forceinline__ float lane_max8(const f32x4& a, const f32x4& b) {
   float r, t;
-  asm("v_max3_f32 %0, %2, %3, %4\n\t"
+  asm("s_nop 7\n\t"
+      "v_max3_f32 %0, %2, %3, %4\n\t"
       "v_max3_f32 %1, %5, %6, %7\n\t"
       "v_max3_f32 %0, %0, %8, %9\n\t"
       "v_max_f32 %0, %0, %1"

@@ -42,6 +42,10 @@ def _case(name):
         "bq64_bkv32_d64_bf16": (1, 2, 700, 64, 64, 32, "bf16", 25, 0.10, 0.40),
         "bq64_bkv32_f32": (1, 2, 600, 64, 64, 32, "f32", 26, 0.15, 0.50),
         "bq256_bkv128_f32": (1, 2, 600, 128, 256, 128, "f32", 27, 0.25, 0.50),
+        # 64-row query tiles at D = 128 (the forward's four-workgroup form: two and four
+        # 32-key steps per mask block)
+        "bq64_bf16": (1, 2, 1000, 128, 64, 64, "bf16", 28, 0.10, 0.50),
+        "bq64_bkv128_bf16": (1, 2, 900, 128, 64, 128, "bf16", 29, 0.15, 0.50),
     }[name]
     B, H, N, D, BQ, BKV, dt, seed, k, p = spec
     return synth.sink_inputs(B, H, N, D, 64, seed=seed, dtype=dt), BQ, BKV, k, p
@@ -50,7 +54,8 @@ def _case(name):
 CASES = ["tiny_fp32", "ragged_bf16", "ragged_bf16_d64", "ragged_f32_d128",
          "ragged_f32_d64_bq128", "single_block", "one_row", "mid_bf16",
          "bkv32_bf16", "bkv128_bf16", "bq256_bf16", "bq256_bkv128_d64_bf16",
-         "bq64_bkv32_d64_bf16", "bq64_bkv32_f32", "bq256_bkv128_f32"]
+         "bq64_bkv32_d64_bf16", "bq64_bkv32_f32", "bq256_bkv128_f32", "bq64_bf16",
+         "bq64_bkv128_bf16"]
 _CACHE = {}
 
 
@@ -242,7 +247,7 @@ def test_end_to_end_mask_fwd_bwd(name):
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_bf16_d64", "bkv32_bf16",
-                                  "bkv128_bf16", "bq256_bkv128_f32"])
+                                  "bkv128_bf16", "bq256_bkv128_f32", "bq64_bf16"])
 def test_dense_path(name):
     """mask = NULL runs every block; it equals the all-ones mask bit for bit and the
     oracle's dense attention."""
