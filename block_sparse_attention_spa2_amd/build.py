@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -28,16 +29,44 @@ FLAGS = [
 SOURCES = ["mask.hip", "fwd.hip", "bwd.hip", "diag.hip", "api.cpp"]
 
 
+# the compiler's per-kernel resource report (registers, spills, LDS), read by _spills
+REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def _spills(text: str) -> list:
+    """(kernel, spilled VGPRs) for every kernel of a resource report that spills."""
+    found, name = [], None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+VGPRs Spill: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            found.append((name, int(m.group(1))))
+    return found
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *REMARKS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(x for x in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in x)
+    text = r.stdout + r.stderr
+    out = "\n".join(x for x in text.splitlines()
+                    if "packed-fp32-ops" not in x and "remark:" not in x)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+    # The bf16 and mask kernels are sized to keep every value in registers (the forward's
+    # launch bounds ask for three workgroups per CU, at most 168 registers): a spill to
+    # scratch memory would cost far more than it saves, so it is a build error. The fp32
+    # attention kernels (first template argument float, mangled "kernelIf") are the
+    # precision path and do spill at D = 128.
+    spills = [(n, c) for n, c in _spills(text) if "kernelIf" not in n]
+    if spills:
+        raise RuntimeError(f"register spills in {src}: " +
+                           ", ".join(f"{n} ({c} VGPRs)" for n, c in spills))
     return obj
 
 

@@ -265,3 +265,21 @@ def test_misaligned_pointers():
     assert L.spa2_select(d, ODD4, 0.1, 0.5, C.byref(bm()), None) == _lib.E_ALIGN
     assert L.spa2_pool(d, FAKE, ODD, FAKE, FAKE, None) == _lib.E_ALIGN
     assert L.spa2_mask_lists(d, C.byref(bm(row_cnt=ODD4)), None) == _lib.E_ALIGN
+
+
+def test_build_rejects_register_spills():
+    """The build reads the compiler's per-kernel resource report and names every kernel
+    that spills vector registers (a build error for all but the fp32 attention kernels)."""
+    from block_sparse_attention_spa2_amd import build
+    report = "\n".join([
+        "fwd.hip:9:1: remark: Function Name: _ZN4spa210fwd_kernelIDF16bLi128E",
+        "fwd.hip:9:1: remark:     VGPRs: 168",
+        "fwd.hip:9:1: remark:     VGPRs Spill: 0",
+        "bwd.hip:5:1: remark: Function Name: _ZN4spa213bwd_dq_kernelIDF16bLi128E",
+        "bwd.hip:5:1: remark:     VGPRs Spill: 12",
+        "bwd.hip:7:1: remark: Function Name: _ZN4spa215bwd_dkdv_kernelIfLi128E",
+        "bwd.hip:7:1: remark:     VGPRs Spill: 104",
+    ])
+    assert build._spills(report) == [("_ZN4spa213bwd_dq_kernelIDF16bLi128E", 12),
+                                     ("_ZN4spa215bwd_dkdv_kernelIfLi128E", 104)]
+    assert build._spills("") == []
