@@ -122,8 +122,8 @@ __global__ __launch_bounds__(64 * NW, (fwd_wgs_per_cu<T, D, BQ, BKV>())) void fw
   using KV = Tile<T, BKV, D>;
   // Two stages in two separate LDS variables: every access names one of them statically
   // (the loop below is unrolled by two), so the compiler can tell that the loads into one
-  // stage do not alias the reads of the other and does not wait for them early.
-  // the epilogue stages half the fp32 O tile in each stage
+  // stage do not alias the reads of the other and does not wait for them early. The
+  // epilogue passes the fp32 O tile through the two stages.
   constexpr int kStageBytes = 2 * KV::kBytes;
   __shared__ __attribute__((aligned(1024))) char stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char stage1[kStageBytes];
