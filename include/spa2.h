@@ -33,8 +33,9 @@
  *     B*H*max(T_m, T_n) <= 2^26. The method's sizes
  *     are BQ = 128, BKV = 64; the others are the block-size variants the pages suggest
  *     trying (rainbus summary, "局限与改进": fixed block sizes are a limitation). The
- *     attention kernels work on tiles of at most 128 rows and 64 keys, so a 256-row or
- *     128-key block is processed as two tiles (same result, same lists).
+ *     attention kernels work on tiles of at most 128 rows and 64 keys (the bf16 forward
+ *     at D = 128 on 32-key steps), so a larger block is processed as several tiles (same
+ *     lists; mask = NULL and an all-ones mask give the same bits).
  *   - Attention is non-causal; the scale is 1/sqrt(D); LSE is the natural-log
  *     log-sum-exp of the scaled scores over the kept keys. Outputs are rounded to the
  *     input dtype (round to nearest even) from fp32 accumulators. A query row whose
