@@ -247,7 +247,8 @@ def test_end_to_end_mask_fwd_bwd(name):
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "ragged_bf16_d64", "bkv32_bf16",
-                                  "bkv128_bf16", "bq256_bkv128_f32", "bq64_bf16"])
+                                  "bkv128_bf16", "bq256_bkv128_f32", "bq64_bf16",
+                                  "bq64_bkv128_bf16", "bq256_bf16", "bq256_bkv128_d64_bf16"])
 def test_dense_path(name):
     """mask = NULL runs every block; it equals the all-ones mask bit for bit and the
     oracle's dense attention."""
