@@ -314,10 +314,11 @@ def test_empty_rows():
         gu.check_close(nm, gu.to_f64(got), want, "bf16", block=blk)
 
 
-def test_deterministic_and_in_bounds():
+@pytest.mark.parametrize("name", ["ragged_bf16", "bq64_bf16", "bkv128_bf16"])
+def test_deterministic_and_in_bounds(name):
     """Two runs are bitwise identical, and nothing is written past the outputs (guard
     regions after each output stay intact; NaN-prefilled outputs are fully overwritten)."""
-    r = ref("ragged_bf16")
+    r = ref(name)
     d = r["dev"]
     B, H, N, D = r["inp"].q.shape
     guard = 4096
